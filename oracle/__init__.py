@@ -1,0 +1,220 @@
+"""fp64 CPU oracle for sliding-window attention (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never imports it and
+shares no code with it.
+
+``swa_oracle.c`` holds the arithmetic (see its header for the definition and
+the passages it follows); this module only builds it with gcc and marshals
+numpy arrays into it.  ``bruteforce.py`` holds a second, independent dense-mask
+formulation used to pin the C oracle on tiny inputs.
+
+Inputs are passed as numpy arrays: float32, or bfloat16 given as raw uint16
+bit patterns (the oracle widens both to double exactly).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "swa_oracle.c")
+_LIB_DIR = os.path.join(_HERE, "_build")
+_LIB = os.path.join(_LIB_DIR, "libswa_oracle.so")
+
+DT_F32 = 0
+DT_BF16 = 1
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle C source into a shared library with gcc (OpenMP, -O2)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_input(x: np.ndarray) -> tuple[np.ndarray, int]:
+    """float32 -> (array, DT_F32); uint16 bf16 bit patterns -> (array, DT_BF16)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, DT_F32
+    if x.dtype == np.uint16:
+        return x, DT_BF16
+    raise TypeError(f"oracle inputs must be float32 or bf16 bits (uint16), got {x.dtype}")
+
+
+def _globals(global_idx) -> tuple[np.ndarray, int]:
+    if global_idx is None:
+        return np.zeros(1, np.int32), 0
+    g = np.ascontiguousarray(np.asarray(global_idx, dtype=np.int32).reshape(-1))
+    return (g if g.size else np.zeros(1, np.int32)), int(g.size)
+
+
+class OracleLib:
+    """One compiled copy of the oracle (the default one, or a test's variant)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_attended_set.argtypes = [I64, I64, I64, I64, I64, P, I64, P]
+        lib.oracle_attended_set.restype = I64
+        lib.oracle_fwd_rows.argtypes = [P, P, P, I, I64, I64, I64, I64, I64, I64, I64, I64,
+                                        P, I64, D, P, I64, P, P]
+        lib.oracle_fwd_rows.restype = I
+        lib.oracle_fwd.argtypes = [P, P, P, I, I64, I64, I64, I64, I64, I64, I64, I64,
+                                   P, I64, D, P, P]
+        lib.oracle_fwd.restype = I
+        lib.oracle_kv_append.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I]
+        lib.oracle_kv_append.restype = I
+        lib.oracle_decode.argtypes = [P, P, P, I, P, P, I64, I64, I64, I64, I64, D, P, P]
+        lib.oracle_decode.restype = I
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = I
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def attended_set(self, i: int, N: int, win_left: int, win_right: int,
+                     dilation: int = 1, global_idx=None) -> list:
+        """S(i) as a sorted list of key positions."""
+        g, ng = _globals(global_idx)
+        buf = np.zeros(N + win_left + win_right + ng + 1, np.int64)
+        n = self.lib.oracle_attended_set(i, N, win_left, win_right, dilation, _ptr(g), ng,
+                                         _ptr(buf))
+        if n < 0:
+            raise ValueError("invalid arguments to oracle_attended_set")
+        return buf[:n].tolist()
+
+    def fwd(self, q, k, v, *, win_left: int, win_right: int = 0, dilation: int = 1,
+            global_idx=None, scale=None):
+        """All rows.  q [B,N,Hq,D], k/v [B,N,Hkv,D] -> (out [B,N,Hq,D], lse [B,Hq,N])."""
+        q, dt = _as_input(q)
+        k, dtk = _as_input(k)
+        v, dtv = _as_input(v)
+        if not dt == dtk == dtv:
+            raise TypeError("q, k and v must share one element type")
+        B, N, Hq, D = q.shape
+        Hkv = k.shape[2]
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        g, ng = _globals(global_idx)
+        out = np.zeros((B, N, Hq, D), np.float64)
+        lse = np.zeros((B, Hq, N), np.float64)
+        rc = self.lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, N, D,
+                                 win_left, win_right, dilation, _ptr(g), ng, float(scale),
+                                 _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_fwd")
+        return out, lse
+
+    def fwd_rows(self, q, k, v, rows, *, win_left: int, win_right: int = 0,
+                 dilation: int = 1, global_idx=None, scale=None):
+        """Selected rows: rows is an [R,3] int array of (b, h, i).
+        Returns (out [R,D], lse [R])."""
+        q, dt = _as_input(q)
+        k, _ = _as_input(k)
+        v, _ = _as_input(v)
+        B, N, Hq, D = q.shape
+        Hkv = k.shape[2]
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        g, ng = _globals(global_idx)
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        out = np.zeros((rows.shape[0], D), np.float64)
+        lse = np.zeros(rows.shape[0], np.float64)
+        rc = self.lib.oracle_fwd_rows(_ptr(q), _ptr(k), _ptr(v), dt, B, Hq, Hkv, N, D,
+                                      win_left, win_right, dilation, _ptr(g), ng,
+                                      float(scale), _ptr(rows), rows.shape[0], _ptr(out),
+                                      _ptr(lse))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_fwd_rows")
+        return out, lse
+
+    def ring(self, kcache, vcache, ring_head, cache_len) -> "Ring":
+        return Ring(self, kcache, vcache, ring_head, cache_len)
+
+
+class Ring:
+    """The oracle's own copy of a ring-buffer KV cache.
+
+    kcache/vcache [B,Hkv,W,D] (float32 or bf16 bits), ring_head/cache_len [B].
+    """
+
+    def __init__(self, orc: OracleLib, kcache, vcache, ring_head, cache_len):
+        self.orc = orc
+        self.k, self.dtype = _as_input(np.array(kcache, copy=True))
+        self.v, _ = _as_input(np.array(vcache, copy=True))
+        self.head = np.ascontiguousarray(np.asarray(ring_head, dtype=np.int64).copy())
+        self.len = np.ascontiguousarray(np.asarray(cache_len, dtype=np.int64).copy())
+        self.B, self.Hkv, self.W, self.D = self.k.shape
+
+    def append(self, k_new, v_new):
+        k_new, _ = _as_input(k_new)
+        v_new, _ = _as_input(v_new)
+        rc = self.orc.lib.oracle_kv_append(_ptr(self.k), _ptr(self.v), _ptr(k_new),
+                                           _ptr(v_new), _ptr(self.head), _ptr(self.len),
+                                           self.B, self.Hkv, self.W, self.D, self.dtype)
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_kv_append")
+
+    def decode(self, q, scale=None):
+        """q [B,Hq,D] -> (out [B,Hq,D], lse [B,Hq]) fp64."""
+        q, _ = _as_input(q)
+        B, Hq, D = q.shape
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        out = np.zeros((B, Hq, D), np.float64)
+        lse = np.zeros((B, Hq), np.float64)
+        rc = self.orc.lib.oracle_decode(_ptr(q), _ptr(self.k), _ptr(self.v), self.dtype,
+                                        _ptr(self.head), _ptr(self.len), B, Hq, self.Hkv,
+                                        self.W, D, float(scale), _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_decode")
+        return out, lse
+
+
+_default = None
+
+
+def default() -> OracleLib:
+    """The oracle built from swa_oracle.c (compiled on first use if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _default = OracleLib(_LIB)
+    return _default
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def attended_set(*a, **kw):
+    return default().attended_set(*a, **kw)
+
+
+def fwd(*a, **kw):
+    return default().fwd(*a, **kw)
+
+
+def fwd_rows(*a, **kw):
+    return default().fwd_rows(*a, **kw)
+
+
+def ring(*a, **kw) -> Ring:
+    return default().ring(*a, **kw)

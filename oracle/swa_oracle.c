@@ -1,0 +1,306 @@
+/*
+ * swa_oracle.c -- plain fp64 CPU oracle for sliding-window attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the independent reference that the
+ * GPU library is checked against.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it.  It shares no code, header,
+ * table or helper with the HIP library, and the HIP library never calls it.
+ *
+ * What it computes (all arithmetic in IEEE double):
+ *
+ *   For query row i of batch b and query head h, with kv head
+ *   kh = h / (Hq / Hkv), the attended set S(i) is
+ *     - Band(i) = { i + t*dil : -wl <= t <= wr } clipped to [0, N)
+ *       (the window around each query, truncated at the sequence edges:
+ *        bmjup.com "Sliding window attention", section "core principle /
+ *        mathematical form"; the dilated index sets i +- t*d:
+ *        mhpn.cn "Dilated sliding window", section 2 "structure comparison"),
+ *     - united with every global position g (g <= i when causal), and
+ *     - if i itself is global, every key j (j <= i when causal)
+ *       (global tokens attend to all positions and all positions attend to
+ *        them: aiqz.cc "Sliding window attention: Mistral", section
+ *        "global attention tokens"; mhpn.cn section 3 "attention sink").
+ *   The call is causal exactly when wr == 0 (a left-only window: bmjup.com,
+ *   section "bidirectional vs unidirectional sliding window").
+ *   S(i) is a set: a key that is both in the band and global counts once.
+ *
+ *     s_j   = scale * sum_c q[b,i,h,c] * k[b,j,kh,c]
+ *     M     = max_{j in S(i)} s_j
+ *     L     = sum_{j in S(i)} exp(s_j - M)
+ *     out   = sum_{j in S(i)} exp(s_j - M) * v[b,j,kh,:] / L
+ *     lse   = M + log(L)
+ *   which is y_i = sum_j softmax(q_i.k_j / sqrt(d)) v_j over the window
+ *   (bmjup.com, "mathematical form"), with the max subtracted before the
+ *   exponential as in the numpy decode demo (aiqz.cc, "Python demo").
+ *   Excluding a key is the same as giving it a score of -infinity before the
+ *   softmax (bmjup.com, section 2 "mask implementation").
+ *
+ * Decode over a ring-buffer KV cache (intelliparadigm.com, section 3.1
+ * "cache mechanism", the RingBuffer class: write at idx % size, then idx += 1;
+ * aiqz.cc, "inference optimisation": the cache keeps only the last W entries):
+ *   append writes slot ring_head, then ring_head = (ring_head + 1) % W and
+ *   cache_len = min(cache_len + 1, W).  A decode step attends the new query
+ *   over the valid slots { (ring_head - 1 - a) mod W : 0 <= a < cache_len },
+ *   i.e. the last cache_len appended entries, the newest included (aiqz.cc
+ *   demo: keys are the last window_size entries, current token included).
+ *
+ * Layouts (row-major): q,out [B,N,Hq,D]; k,v [B,N,Hkv,D]; lse [B,Hq,N];
+ * decode q,out [B,Hq,D]; kcache,vcache [B,Hkv,W,D]; decode lse [B,Hq].
+ * Element types of the inputs: 0 = float32, 1 = bfloat16 (raw 16-bit
+ * patterns).  Values are widened to double exactly.
+ *
+ * Parity pins: see tests/test_oracle_pins.py (dense-mask brute force, the
+ * dilated index sets printed on the dilated-window page, closed forms and
+ * invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- element access: exact widening to double ------------------------ */
+
+static double load_elem(const void* base, int dtype, int64_t idx) {
+    if (dtype == 0) return (double)((const float*)base)[idx];
+    /* bfloat16: the upper half of an IEEE float32 */
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static void copy_elem(void* dst, const void* src, int dtype, int64_t di, int64_t si) {
+    if (dtype == 0) ((float*)dst)[di] = ((const float*)src)[si];
+    else ((uint16_t*)dst)[di] = ((const uint16_t*)src)[si];
+}
+
+/* ---- the attended set S(i) ------------------------------------------- */
+
+static int cmp_int64(const void* a, const void* b) {
+    int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Sorted, duplicate-free copy of the global positions.  Returns the count. */
+static int64_t normalise_globals(const int32_t* g, int64_t ng, int64_t* out) {
+    for (int64_t t = 0; t < ng; t++) out[t] = g[t];
+    qsort(out, (size_t)ng, sizeof(int64_t), cmp_int64);
+    int64_t m = 0;
+    for (int64_t t = 0; t < ng; t++)
+        if (m == 0 || out[t] != out[m - 1]) out[m++] = out[t];
+    return m;
+}
+
+static int is_member(const int64_t* sorted, int64_t n, int64_t x) {
+    for (int64_t t = 0; t < n; t++)
+        if (sorted[t] == x) return 1;
+    return 0;
+}
+
+/* Fills idx (capacity N) with S(i) in increasing order; returns |S(i)|. */
+static int64_t attended_set(int64_t i, int64_t N, int64_t wl, int64_t wr, int64_t dil,
+                            const int64_t* G, int64_t nG, int64_t* idx) {
+    const int causal = (wr == 0);
+    int64_t n = 0;
+    if (is_member(G, nG, i)) {
+        for (int64_t j = 0; j < N; j++)
+            if (!causal || j <= i) idx[n++] = j;
+        return n;
+    }
+    for (int64_t t = -wl; t <= wr; t++) {
+        int64_t j = i + t * dil;
+        if (j >= 0 && j < N) idx[n++] = j;
+    }
+    for (int64_t t = 0; t < nG; t++)
+        if (!causal || G[t] <= i) idx[n++] = G[t];
+    qsort(idx, (size_t)n, sizeof(int64_t), cmp_int64);
+    int64_t m = 0;
+    for (int64_t t = 0; t < n; t++)
+        if (m == 0 || idx[t] != idx[m - 1]) idx[m++] = idx[t];
+    return m;
+}
+
+/* Public: S(i) as int64 positions.  Returns |S(i)|, or -1 on bad input. */
+int64_t oracle_attended_set(int64_t i, int64_t N, int64_t wl, int64_t wr, int64_t dil,
+                            const int32_t* gidx, int64_t ng, int64_t* out_idx) {
+    if (N <= 0 || i < 0 || i >= N || wl < 0 || wr < 0 || dil < 1 || ng < 0) return -1;
+    int64_t* G = (int64_t*)malloc(sizeof(int64_t) * (size_t)(ng > 0 ? ng : 1));
+    int64_t nG = normalise_globals(gidx, ng, G);
+    int64_t n = attended_set(i, N, wl, wr, dil, G, nG, out_idx);
+    free(G);
+    return n;
+}
+
+/* ---- one softmax-attention row over an explicit key list ------------- */
+
+/* qrow: pointer-free access through (base, dtype, offset, stride 1).
+ * Keys/values: element (j, c) at kbase + j*kstride + c. */
+static void attend_row(const void* q, int64_t qoff, const void* k, const void* v,
+                       int64_t kvoff, int64_t kvstride, int dtype, int64_t D,
+                       const int64_t* keys, int64_t nkeys, double scale,
+                       double* s /* scratch, nkeys */, double* out, double* lse) {
+    double M = -INFINITY;
+    for (int64_t t = 0; t < nkeys; t++) {
+        double dot = 0.0;
+        int64_t ko = kvoff + keys[t] * kvstride;
+        for (int64_t c = 0; c < D; c++)
+            dot += load_elem(q, dtype, qoff + c) * load_elem(k, dtype, ko + c);
+        s[t] = scale * dot;
+        if (s[t] > M) M = s[t];
+    }
+    double L = 0.0;
+    for (int64_t c = 0; c < D; c++) out[c] = 0.0;
+    for (int64_t t = 0; t < nkeys; t++) {
+        double p = exp(s[t] - M);
+        L += p;
+        int64_t vo = kvoff + keys[t] * kvstride;
+        for (int64_t c = 0; c < D; c++) out[c] += p * load_elem(v, dtype, vo + c);
+    }
+    for (int64_t c = 0; c < D; c++) out[c] /= L;
+    *lse = M + log(L);
+}
+
+/* ---- forward --------------------------------------------------------- */
+
+static int fwd_args_ok(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                       int64_t wl, int64_t wr, int64_t dil, int dtype) {
+    return B > 0 && Hq > 0 && Hkv > 0 && N > 0 && D > 0 && Hq % Hkv == 0 &&
+           wl >= 0 && wr >= 0 && dil >= 1 && (dtype == 0 || dtype == 1);
+}
+
+/* Computes rows (b, h, i) listed in rows[3*r .. 3*r+2] into
+ * out_rows[r*D .. r*D+D-1] and lse_rows[r].  Returns 0, or -1 on bad input. */
+int oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                    int64_t wl, int64_t wr, int64_t dil,
+                    const int32_t* gidx, int64_t ng, double scale,
+                    const int64_t* rows, int64_t n_rows,
+                    double* out_rows, double* lse_rows) {
+    if (!fwd_args_ok(B, Hq, Hkv, N, D, wl, wr, dil, dtype)) return -1;
+    for (int64_t t = 0; t < ng; t++)
+        if (gidx[t] < 0 || gidx[t] >= N) return -1;
+    for (int64_t r = 0; r < n_rows; r++)
+        if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 ||
+            rows[3 * r + 1] >= Hq || rows[3 * r + 2] < 0 || rows[3 * r + 2] >= N)
+            return -1;
+    int64_t* G = (int64_t*)malloc(sizeof(int64_t) * (size_t)(ng > 0 ? ng : 1));
+    int64_t nG = normalise_globals(gidx, ng, G);
+    const int64_t group = Hq / Hkv;
+
+#pragma omp parallel
+    {
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + wl + wr + nG + 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(N + wl + wr + nG + 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; r++) {
+            int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            int64_t kh = h / group;
+            int64_t nk = attended_set(i, N, wl, wr, dil, G, nG, keys);
+            int64_t qoff = ((b * N + i) * Hq + h) * D;
+            int64_t kvoff = (b * N * Hkv + kh) * D; /* key j at kvoff + j*Hkv*D */
+            attend_row(q, qoff, k, v, kvoff, Hkv * D, dtype, D, keys, nk, scale, s,
+                       out_rows + r * D, lse_rows + r);
+        }
+        free(keys);
+        free(s);
+    }
+    free(G);
+    return 0;
+}
+
+/* All rows: out [B,N,Hq,D] and lse [B,Hq,N] in double. */
+int oracle_fwd(const void* q, const void* k, const void* v, int dtype,
+               int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+               int64_t wl, int64_t wr, int64_t dil,
+               const int32_t* gidx, int64_t ng, double scale,
+               double* out, double* lse) {
+    if (!fwd_args_ok(B, Hq, Hkv, N, D, wl, wr, dil, dtype)) return -1;
+    int64_t n_rows = B * N * Hq;
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * 3 * (size_t)n_rows);
+    double* lse_rows = (double*)malloc(sizeof(double) * (size_t)n_rows);
+    /* row order (b, i, h) matches the out layout [B,N,Hq,D] */
+    int64_t r = 0;
+    for (int64_t b = 0; b < B; b++)
+        for (int64_t i = 0; i < N; i++)
+            for (int64_t h = 0; h < Hq; h++) {
+                rows[3 * r] = b; rows[3 * r + 1] = h; rows[3 * r + 2] = i; r++;
+            }
+    int rc = oracle_fwd_rows(q, k, v, dtype, B, Hq, Hkv, N, D, wl, wr, dil, gidx, ng,
+                             scale, rows, n_rows, out, lse_rows);
+    if (rc == 0)
+        for (r = 0; r < n_rows; r++) {
+            int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            lse[(b * Hq + h) * N + i] = lse_rows[r];
+        }
+    free(rows);
+    free(lse_rows);
+    return rc;
+}
+
+/* ---- ring-buffer KV cache -------------------------------------------- */
+
+/* Appends k_new, v_new [B,Hkv,D] into kcache, vcache [B,Hkv,W,D] (element type
+ * dtype) at slot ring_head[b], then advances ring_head and cache_len. */
+int oracle_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new,
+                     int64_t* ring_head, int64_t* cache_len,
+                     int64_t B, int64_t Hkv, int64_t W, int64_t D, int dtype) {
+    if (B <= 0 || Hkv <= 0 || W <= 0 || D <= 0 || (dtype != 0 && dtype != 1)) return -1;
+    for (int64_t b = 0; b < B; b++) {
+        if (ring_head[b] < 0 || ring_head[b] >= W || cache_len[b] < 0 || cache_len[b] > W)
+            return -1;
+        int64_t slot = ring_head[b];
+        for (int64_t h = 0; h < Hkv; h++)
+            for (int64_t c = 0; c < D; c++) {
+                int64_t di = ((b * Hkv + h) * W + slot) * D + c;
+                int64_t si = (b * Hkv + h) * D + c;
+                copy_elem(kcache, k_new, dtype, di, si);
+                copy_elem(vcache, v_new, dtype, di, si);
+            }
+        ring_head[b] = (slot + 1) % W;
+        cache_len[b] = cache_len[b] + 1 < W ? cache_len[b] + 1 : W;
+    }
+    return 0;
+}
+
+/* One decode step for every (b, h): q [B,Hq,D] over the valid ring slots.
+ * out [B,Hq,D] and lse [B,Hq] in double.  Rows with cache_len == 0 have no
+ * keys; they are reported as an error (-1). */
+int oracle_decode(const void* q, const void* kcache, const void* vcache, int dtype,
+                  const int64_t* ring_head, const int64_t* cache_len,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t W, int64_t D, double scale,
+                  double* out, double* lse) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || D <= 0 ||
+        (dtype != 0 && dtype != 1))
+        return -1;
+    for (int64_t b = 0; b < B; b++)
+        if (ring_head[b] < 0 || ring_head[b] >= W || cache_len[b] < 1 || cache_len[b] > W)
+            return -1;
+    const int64_t group = Hq / Hkv;
+#pragma omp parallel
+    {
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+        double* s = (double*)malloc(sizeof(double) * (size_t)W);
+#pragma omp for schedule(static)
+        for (int64_t bh = 0; bh < B * Hq; bh++) {
+            int64_t b = bh / Hq, h = bh % Hq, kh = h / group;
+            int64_t n = cache_len[b];
+            for (int64_t a = 0; a < n; a++) keys[a] = ((ring_head[b] - 1 - a) % W + W) % W;
+            int64_t qoff = (b * Hq + h) * D;
+            int64_t kvoff = (b * Hkv + kh) * W * D; /* slot j at kvoff + j*D */
+            attend_row(q, qoff, kcache, vcache, kvoff, D, dtype, D, keys, n, scale, s,
+                       out + bh * D, lse + bh);
+        }
+        free(keys);
+        free(s);
+    }
+    return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,333 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Every function here takes an ``OracleLib`` and raises AssertionError when the
+oracle disagrees with what the pages or the mathematics fix:
+
+* values the pages print (index sets, the ring-buffer rule, the demo's window),
+  stored under tests/golden/ with their citations;
+* the dense-mask brute force (a different formulation of the same definition);
+* closed forms and special cases that reduce to a library routine
+  (torch's scaled_dot_product_attention in float64 on the CPU);
+* invariants (dilation = strided undilated problems, GQA = repeated heads,
+  ring rotation, partial rings).
+
+The same functions run against deliberately broken copies of the oracle in
+test_oracle_mutations.py, to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import bruteforce
+from sliding_window_attention_tiled_amd.inputs import fwd_inputs, to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close(a, b, tol, what):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+    assert err <= tol, f"{what}: max abs diff {err:.3e} > {tol:.1e}"
+
+
+def _sdpa(q, k, v, causal, scale):
+    """Library attention in float64: q/k/v [B,N,H,D] float64 numpy (H equal)."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3)))
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v),
+                                                         is_causal=causal, scale=scale)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+# ---- values printed on the pages -------------------------------------------
+
+def pin_dilated_index_sets(orc):
+    g = _golden("dilated_index_sets.json")
+    i, N = 40, 100
+    for c in g["cases"]:
+        got = orc.attended_set(i, N, g["win_left"], g["win_right"], c["dilation"])
+        assert got == [i + o for o in c["offsets"]], (c, got)
+
+
+def pin_dilated_span(orc):
+    g = _golden("dilated_span.json")
+    i, N = 50, 100
+    got = orc.attended_set(i, N, g["win_left"], g["win_right"], g["dilation"])
+    assert len(got) == g["keys"], got
+    assert got[-1] - got[0] + 1 == g["span"], got
+
+
+def pin_edge_truncation(orc):
+    g = _golden("edge_truncation.json")
+    half = g["W"] // 2
+    for c in g["cases"]:
+        got = orc.attended_set(c["i"], g["N"], half, half, 1)
+        assert got == c["keys"], (c, got)
+
+
+def pin_decode_demo_window(orc):
+    g = _golden("decode_demo_window.json")
+    n, w = g["n"], g["window_size"]
+    # as a causal forward window of w keys for the last token
+    assert orc.attended_set(n - 1, n, w - 1, 0, 1) == g["keys"]
+    # as a decode step: a ring of w slots after appending n tokens one by one,
+    # scale 1 as in the demo.  The demo draws K, V, q from seed 42.
+    rs = np.random.RandomState(42)
+    d = 8
+    K = rs.randn(n, d).astype(np.float32)
+    V = rs.randn(n, d).astype(np.float32)
+    q = rs.randn(d).astype(np.float32)
+    ring = orc.ring(np.zeros((1, 1, w, d), np.float32), np.zeros((1, 1, w, d), np.float32),
+                    [0], [0])
+    for t in range(n):
+        ring.append(K[t][None, None, :], V[t][None, None, :])
+    out, lse = ring.decode(q[None, None, :], scale=1.0)
+    keys = g["keys"]
+    ref = _sdpa(q[None, None, None, :].astype(np.float64),
+                K[keys][None, :, None, :].astype(np.float64),
+                V[keys][None, :, None, :].astype(np.float64), False, 1.0)
+    _close(out[0, 0], ref[0, 0, 0], 1e-12, "decode demo window")
+    s = K[keys].astype(np.float64) @ q.astype(np.float64)
+    _close(lse[0, 0], np.log(np.exp(s).sum()), 1e-12, "decode demo lse")
+
+
+def pin_ring_buffer_trace(orc):
+    g = _golden("ring_buffer_trace.json")
+    W = g["size"]
+    ring = orc.ring(np.zeros((1, 1, W, 1), np.float32), np.zeros((1, 1, W, 1), np.float32),
+                    [0], [0])
+    for item in g["appended"]:
+        x = np.full((1, 1, 1), float(item), np.float32)
+        ring.append(x, x)
+    assert ring.k[0, 0, :, 0].tolist() == [float(x) for x in g["buffer"]], ring.k
+    assert int(ring.head[0]) == g["next_slot"]
+    assert int(ring.len[0]) == W
+    # q = 0: uniform weights over the held items -> their mean, lse = ln(count)
+    out, lse = ring.decode(np.zeros((1, 1, 1), np.float32), scale=1.0)
+    _close(out[0, 0, 0], np.mean(g["held_items"]), 1e-12, "ring mean")
+    _close(lse[0, 0], math.log(len(g["held_items"])), 1e-12, "ring lse")
+
+
+# ---- the dense-mask brute force ---------------------------------------------
+
+BRUTE_CASES = [
+    # (B, Hq, Hkv, N, D, wl, wr, dil, globals, dtype, scale)
+    (1, 2, 2, 1, 8, 3, 0, 1, None, "f32", None),
+    (1, 2, 2, 2, 8, 3, 0, 1, None, "f32", None),
+    (2, 2, 1, 63, 16, 7, 0, 1, None, "bf16", None),
+    (1, 4, 2, 70, 8, 5, 3, 1, None, "f32", 0.37),           # asymmetric window
+    (1, 2, 2, 65, 8, 4, 4, 1, [0, 17, 17, 64], "bf16", None),  # bidir + globals
+    (1, 2, 2, 64, 8, 9, 0, 1, [0, 31, 40], "f32", None),      # causal + globals
+    (1, 2, 2, 77, 8, 5, 0, 3, None, "bf16", None),            # dilated causal
+    (1, 2, 2, 81, 8, 2, 3, 2, [5, 6], "f32", None),           # dilated bidir + globals
+    (1, 4, 1, 257, 16, 20, 0, 4, None, "bf16", 0.2),          # GQA 4, dilated
+    (1, 2, 2, 40, 8, 100, 100, 1, None, "f32", None),         # window > N
+]
+
+
+def pin_bruteforce(orc):
+    for n, (B, Hq, Hkv, N, D, wl, wr, dil, G, dt, sc) in enumerate(BRUTE_CASES):
+        q, k, v = fwd_inputs(100 + n, B, Hq, Hkv, N, D, dt)
+        o1, l1 = orc.fwd(q, k, v, win_left=wl, win_right=wr, dilation=dil, global_idx=G,
+                         scale=sc)
+        o2, l2 = bruteforce.fwd(q, k, v, win_left=wl, win_right=wr, dilation=dil,
+                                global_idx=G, scale=sc)
+        _close(o1, o2, 1e-12, f"brute force case {n} out")
+        _close(l1, l2, 1e-12, f"brute force case {n} lse")
+        # the row-sampled entry point agrees with the full one
+        rows = np.array([[B - 1, Hq - 1, N - 1], [0, 0, 0], [0, Hq // 2, N // 2]])
+        o3, l3 = orc.fwd_rows(q, k, v, rows, win_left=wl, win_right=wr, dilation=dil,
+                              global_idx=G, scale=sc)
+        for r, (b, h, i) in enumerate(rows):
+            _close(o3[r], o1[b, i, h], 0.0, "fwd_rows out")
+            _close(l3[r], l1[b, h, i], 0.0, "fwd_rows lse")
+
+
+def pin_bruteforce_mask_is_page_mask(orc):
+    """bruteforce's mask for odd W equals the page's |j - i| > W // 2 rule."""
+    del orc
+    for N, W in [(10, 5), (33, 9), (7, 1)]:
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        page_masked = np.abs(j - i) > W // 2
+        assert np.array_equal(~page_masked, bruteforce.mask_matrix(N, W // 2, W // 2))
+
+
+# ---- closed forms and special cases -------------------------------------------
+
+def pin_full_window(orc):
+    """A window covering the whole sequence is ordinary (causal) attention."""
+    for causal in (False, True):
+        B, H, N, D = 2, 3, 37, 16
+        q, k, v = fwd_inputs(7, B, H, H, N, D, "f32")
+        wr = 0 if causal else N
+        out, lse = orc.fwd(q, k, v, win_left=N + 5, win_right=wr, scale=0.3)
+        ref = _sdpa(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                    causal, 0.3)
+        _close(out, ref, 1e-12, f"full window causal={causal}")
+        s = 0.3 * np.einsum("bihd,bjhd->bhij", q.astype(np.float64), k.astype(np.float64))
+        if causal:
+            s = s + np.triu(np.full((N, N), -np.inf), 1)
+        ref_lse = np.log(np.exp(s).sum(-1))
+        _close(lse, ref_lse, 1e-12, f"full window lse causal={causal}")
+
+
+def pin_zero_window(orc):
+    """wl = wr = 0: each query attends only itself -> out_i = v_i, lse_i = s_ii."""
+    B, Hq, Hkv, N, D = 1, 4, 2, 19, 8
+    q, k, v = fwd_inputs(8, B, Hq, Hkv, N, D, "bf16")
+    out, lse = orc.fwd(q, k, v, win_left=0, win_right=0, scale=0.5)
+    qf, kf, vf = (bruteforce.widen(x) for x in (q, k, v))
+    for h in range(Hq):
+        kh = h // (Hq // Hkv)
+        _close(out[:, :, h], vf[:, :, kh], 0.0, "zero window out")
+        s = 0.5 * np.sum(qf[:, :, h] * kf[:, :, kh], axis=-1)
+        _close(lse[:, h], s, 1e-12, "zero window lse")
+
+
+def _count_band(i, N, wl, wr, d):
+    tmin = max(-wl, -(i // d))
+    tmax = min(wr, (N - 1 - i) // d)
+    return list(range(i + tmin * d, i + tmax * d + 1, d))
+
+
+def pin_q_zero(orc):
+    """q = 0: uniform weights -> out = mean of v over S(i), lse = ln |S(i)|."""
+    for (N, wl, wr, d, G) in [(50, 6, 0, 1, None), (50, 3, 4, 3, None),
+                              (60, 5, 0, 2, [0, 13, 14]), (45, 2, 2, 1, [7, 44])]:
+        B, H, D = 1, 2, 4
+        _, k, v = fwd_inputs(9, B, H, H, N, D, "f32")
+        q = np.zeros((B, N, H, D), np.float32)
+        out, lse = orc.fwd(q, k, v, win_left=wl, win_right=wr, dilation=d, global_idx=G)
+        causal = wr == 0
+        gset = set(G or [])
+        for i in range(N):
+            if i in gset:
+                S = [j for j in range(N) if not causal or j <= i]
+            else:
+                S = sorted(set(_count_band(i, N, wl, wr, d)) |
+                           {g for g in gset if not causal or g <= i})
+            _close(out[0, i], v[0, S].astype(np.float64).mean(axis=0), 1e-12, "q=0 mean")
+            _close(lse[0, :, i], math.log(len(S)), 1e-12, "q=0 lse")
+
+
+def pin_dilation_strided(orc):
+    """Dilation d equals d undilated problems on the residue subsequences r::d."""
+    B, H, N, D = 1, 2, 90, 8
+    q, k, v = fwd_inputs(10, B, H, H, N, D, "bf16")
+    for (wl, wr, d) in [(5, 0, 2), (4, 3, 3), (7, 0, 4)]:
+        out, lse = orc.fwd(q, k, v, win_left=wl, win_right=wr, dilation=d)
+        for r in range(d):
+            o_r, l_r = orc.fwd(q[:, r::d], k[:, r::d], v[:, r::d], win_left=wl,
+                               win_right=wr, dilation=1, scale=1 / math.sqrt(D))
+            _close(out[:, r::d], o_r, 1e-12, "dilation strided out")
+            _close(lse[:, :, r::d], l_r, 1e-12, "dilation strided lse")
+        # and each residue subsequence against the library routine when the
+        # window covers it entirely
+        o_all, _ = orc.fwd(q, k, v, win_left=N, win_right=0, dilation=d)
+        for r in range(d):
+            ref = _sdpa(*(bruteforce.widen(x[:, r::d]) for x in (q, k, v)), True,
+                        1 / math.sqrt(D))
+            _close(o_all[:, r::d], ref, 1e-12, "dilated full window")
+
+
+def pin_gqa(orc):
+    """Grouped KV heads equal running with k, v repeated per query head."""
+    B, Hq, Hkv, N, D = 1, 6, 2, 33, 8
+    q, k, v = fwd_inputs(11, B, Hq, Hkv, N, D, "f32")
+    out, lse = orc.fwd(q, k, v, win_left=4, win_right=2)
+    kr = np.repeat(k, Hq // Hkv, axis=2)
+    vr = np.repeat(v, Hq // Hkv, axis=2)
+    out2, lse2 = orc.fwd(q, kr, vr, win_left=4, win_right=2)
+    _close(out, out2, 0.0, "gqa out")
+    _close(lse, lse2, 0.0, "gqa lse")
+    ref = _sdpa(*(x.astype(np.float64) for x in (q, kr, vr)), True, 1 / math.sqrt(D))
+    out3, _ = orc.fwd(q, k, v, win_left=N, win_right=0)
+    _close(out3, ref, 1e-12, "gqa full causal")
+
+
+def pin_globals(orc):
+    """A global row is a full attention row; with a full window globals change nothing."""
+    B, H, N, D = 1, 2, 48, 8
+    q, k, v = fwd_inputs(12, B, H, H, N, D, "f32")
+    G = [0, 5, 47]
+    for causal in (False, True):
+        wr = 0 if causal else 3
+        out, _ = orc.fwd(q, k, v, win_left=3, win_right=wr, global_idx=G)
+        ref = _sdpa(*(x.astype(np.float64) for x in (q, k, v)), causal, 1 / math.sqrt(D))
+        for g in G:
+            _close(out[:, g], ref[:, g], 1e-12, f"global row {g} causal={causal}")
+        full, _ = orc.fwd(q, k, v, win_left=N, win_right=0 if causal else N, global_idx=G)
+        _close(full, ref, 1e-12, "full window with globals")
+    # causal visibility of a global column: row 2 must not see global key 5
+    assert orc.attended_set(2, N, 1, 0, 1, G) == [0, 1, 2]
+    assert orc.attended_set(10, N, 1, 0, 1, G) == [0, 5, 9, 10]
+    # bidirectional: row 2 sees key 5 and 47 as well
+    assert orc.attended_set(2, N, 1, 1, 1, G) == [0, 1, 2, 3, 5, 47]
+
+
+# ---- decode ---------------------------------------------------------------------
+
+def _logical_sequence(ring_k, ring_v, head, length):
+    """Oldest-to-newest rows of one ring (numpy copy, [length, H, D])."""
+    W = ring_k.shape[1]
+    slots = [(head - length + a) % W for a in range(length)]
+    return ring_k[:, slots].transpose(1, 0, 2), ring_v[:, slots].transpose(1, 0, 2)
+
+
+def pin_decode(orc):
+    """A decode step equals the last row of a causal forward with win_left = W-1
+    over the logical sequence; partial rings equal full causal attention over the
+    filled part; rotating the ring changes nothing."""
+    B, Hq, Hkv, W, D = 3, 4, 2, 8, 8
+    rng = np.random.Generator(np.random.PCG64(13))
+    kc = rng.standard_normal((B, Hkv, W, D), dtype=np.float32)
+    vc = rng.standard_normal((B, Hkv, W, D), dtype=np.float32)
+    head = np.array([0, 3, 7])
+    length = np.array([W, 2, 0])            # full, partial, empty rings
+    ring = orc.ring(to_bf16_bits(kc), to_bf16_bits(vc), head, length)
+    for step in range(11):
+        qt = to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+        kt = to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        vt = to_bf16_bits(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        ring.append(kt, vt)
+        out, lse = ring.decode(qt, scale=0.25)
+        for b in range(B):
+            n = int(ring.len[b])
+            assert n == min(W, int(length[b]) + step + 1)
+            ks, vs = _logical_sequence(ring.k[b], ring.v[b], int(ring.head[b]), n)
+            # newest entry is the one just appended
+            assert np.array_equal(ks[-1], kt[b]) and np.array_equal(vs[-1], vt[b])
+            qs = np.zeros((1, n, Hq, D), np.uint16)
+            qs[0, -1] = qt[b]
+            o_f, l_f = orc.fwd(qs, ks[None], vs[None], win_left=W - 1, win_right=0,
+                               scale=0.25)
+            _close(out[b], o_f[0, -1], 1e-12, "decode vs causal fwd last row")
+            _close(lse[b], l_f[0, :, -1], 1e-12, "decode lse vs causal fwd")
+            kr = np.repeat(bruteforce.widen(ks), Hq // Hkv, axis=1)
+            vr = np.repeat(bruteforce.widen(vs), Hq // Hkv, axis=1)
+            ref = _sdpa(bruteforce.widen(qt[b])[None, None], kr[None], vr[None], False, 0.25)
+            _close(out[b], ref[0, 0], 1e-12, "decode vs library attention")
+    # rotation: the same logical content at another physical offset
+    out_a, lse_a = ring.decode(qt, scale=0.25)
+    rot = 5
+    ring2 = orc.ring(np.roll(ring.k, rot, axis=2), np.roll(ring.v, rot, axis=2),
+                     (ring.head + rot) % W, ring.len)
+    out_b, lse_b = ring2.decode(qt, scale=0.25)
+    _close(out_a, out_b, 1e-12, "ring rotation out")
+    _close(lse_a, lse_b, 1e-12, "ring rotation lse")
+
+
+ALL_PINS = [
+    pin_dilated_index_sets, pin_dilated_span, pin_edge_truncation, pin_decode_demo_window,
+    pin_ring_buffer_trace, pin_bruteforce, pin_bruteforce_mask_is_page_mask, pin_full_window,
+    pin_zero_window, pin_q_zero, pin_dilation_strided, pin_gqa, pin_globals, pin_decode,
+]

@@ -1,0 +1,71 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each case copies oracle/swa_oracle.c, applies one plausible mistake (a dropped
+term, a wrong sign or index, a transposed operand, a wrong ring rule), builds
+the copy with gcc into a temporary directory and runs every pin in
+tests/oracle_pins.py against it.  The test passes when at least one pin fails
+for every mutation; the real oracle is never modified.
+"""
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+MUTATIONS = {
+    "drop_scale": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "band_right_exclusive": ("for (int64_t t = -wl; t <= wr; t++) {",
+                             "for (int64_t t = -wl; t < wr; t++) {"),
+    "band_left_inclusive_extra": ("for (int64_t t = -wl; t <= wr; t++) {",
+                                  "for (int64_t t = -wl - 1; t <= wr; t++) {"),
+    "dilation_sign": ("int64_t j = i + t * dil;", "int64_t j = i - t * dil;"),
+    "dilation_ignored": ("int64_t j = i + t * dil;", "int64_t j = i + t;"),
+    "kv_head_modulo": ("int64_t kh = h / group;\n            int64_t nk",
+                       "int64_t kh = h % Hkv;\n            int64_t nk"),
+    "globals_not_deduplicated": ("if (m == 0 || idx[t] != idx[m - 1]) idx[m++] = idx[t];",
+                                 "idx[m++] = idx[t];"),
+    "global_column_ignores_causal": ("if (!causal || G[t] <= i) idx[n++] = G[t];",
+                                     "idx[n++] = G[t];"),
+    "global_row_not_full": ("if (is_member(G, nG, i)) {", "if (0) {"),
+    "global_row_ignores_causal": ("if (!causal || j <= i) idx[n++] = j;", "idx[n++] = j;"),
+    "lse_without_max": ("*lse = M + log(L);", "*lse = log(L);"),
+    "softmax_sign": ("double p = exp(s[t] - M);", "double p = exp(M - s[t]);"),
+    "no_normalisation": ("for (int64_t c = 0; c < D; c++) out[c] /= L;", ""),
+    "value_reads_key": ("out[c] += p * load_elem(v, dtype, vo + c);",
+                        "out[c] += p * load_elem(k, dtype, vo + c);"),
+    "query_layout_transposed": ("int64_t qoff = ((b * N + i) * Hq + h) * D;",
+                                "int64_t qoff = ((b * Hq + h) * N + i) * D;"),
+    "bf16_widening": ("(uint32_t)((const uint16_t*)base)[idx] << 16;",
+                      "(uint32_t)((const uint16_t*)base)[idx] << 15;"),
+    "ring_order_forward": ("keys[a] = ((ring_head[b] - 1 - a) % W + W) % W;",
+                           "keys[a] = ((ring_head[b] + a) % W + W) % W;"),
+    "ring_head_not_advanced": ("ring_head[b] = (slot + 1) % W;", "ring_head[b] = slot;"),
+    "ring_writes_wrong_slot": ("int64_t slot = ring_head[b];",
+                               "int64_t slot = (ring_head[b] + 1) % W;"),
+    "cache_len_uncapped": ("cache_len[b] = cache_len[b] + 1 < W ? cache_len[b] + 1 : W;",
+                           "cache_len[b] = cache_len[b] + 1;"),
+    "decode_kv_head_modulo": ("int64_t b = bh / Hq, h = bh % Hq, kh = h / group;",
+                              "int64_t b = bh / Hq, h = bh % Hq, kh = h % Hkv;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle._SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, source, tmp_path):
+    old, new = MUTATIONS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name} not unique or missing"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.build(force=True, src=str(src), out=str(tmp_path / "libmutant.so"))
+    orc = oracle.OracleLib(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, IndexError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, f"no pin catches mutation {name}"
