@@ -1,0 +1,174 @@
+/*
+ * swa.h -- C ABI of libswa.so: sliding-window attention for AMD MI355X (gfx950).
+ *
+ * The operation (bmjup.com, "Sliding window attention", section "core
+ * principle", mathematical form): for every query position i,
+ *     y_i = sum_{j in S(i)} softmax_j(scale * q_i . k_j) v_j
+ * where S(i) is the window around i, truncated at the sequence edges.
+ *
+ * Window parameters (explicit left/right extents counted in dilated steps):
+ *   Band(i) = { i + t*dilation : -win_left <= t <= win_right } intersected with [0, N)
+ *   - causal window of W keys, [i-W+1, i]:     win_left = W-1, win_right = 0
+ *     (bmjup.com, "bidirectional vs unidirectional sliding window": a causal
+ *      query sees only keys to its left; aiqz.cc "Python demo": the last
+ *      window_size keys, the current one included)
+ *   - bidirectional odd W, [i-(W-1)/2, i+(W-1)/2]: win_left = win_right = (W-1)/2
+ *   - dilated windows i +- t*d (mhpn.cn "Dilated sliding window", section 2
+ *     "structure comparison"): dilation = d
+ * The call is causal exactly when win_right == 0.
+ *
+ * Global tokens (aiqz.cc, "global attention tokens"; mhpn.cn, section 3,
+ * "attention sink"): a global position g is seen by every query (by queries
+ * i >= g when causal), and a global query row attends to every key (keys
+ * j <= i when causal).  S(i) is a set: a global key inside the band counts
+ * once.
+ *
+ * Decode (intelliparadigm.com, section 3.1 "cache mechanism", RingBuffer:
+ * write buffer[idx % size], then idx += 1; aiqz.cc, "inference optimisation":
+ * the cache keeps only the last W entries): a ring of W slots per sequence.
+ * ring_head[b] is the next slot to write; cache_len[b] (<= W) counts valid
+ * entries.  After an append, the valid slots of sequence b are
+ *     { (ring_head[b] - 1 - a) mod W : 0 <= a < cache_len[b] }.
+ *
+ * Conventions for every entry point:
+ *   - Layouts are row-major and contiguous:
+ *       q, out        [B, N, Hq, D]       (batch, sequence, heads, head dim)
+ *       k, v          [B, N, Hkv, D]
+ *       lse           [B, Hq, N]  float32, natural log of the softmax partition
+ *                     function of the scaled scores
+ *       decode q, out [B, Hq, D];  decode lse [B, Hq] float32
+ *       kcache,vcache [B, Hkv, W, D]
+ *     Query head h reads kv head h / (Hq / Hkv) (grouped-query attention).
+ *   - Element type of q, k, v, out, kcache, vcache, k_new, v_new: `dtype`
+ *     (SWA_F32 or SWA_BF16).  Accumulation is float32.  In bf16 the softmax
+ *     weights are rounded to bf16 (nearest even) before the weighted sum of v.
+ *   - D must be 64 or 128.
+ *   - Device pointers are caller-owned device memory.  The library allocates
+ *     nothing and keeps no state between calls; all work is enqueued on
+ *     `stream` (0 = the null stream) and nothing synchronises the host.
+ *   - Return value: SWA_OK, or a negative status.  Argument errors are found
+ *     before anything is enqueued.  SWA_ERR_HIP reports a launch failure
+ *     (hipGetLastError); faults during execution surface at the caller's next
+ *     synchronisation.  Calls on one stream are ordered; the library is
+ *     thread-safe (stateless).
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+enum {
+    SWA_OK = 0,
+    SWA_ERR_ARG = -1,          /* null pointer, bad size, bad window, bad global index */
+    SWA_ERR_UNSUPPORTED = -2,  /* D not in {64, 128}, unknown dtype, too many globals */
+    SWA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+    SWA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+};
+
+/* Largest number of distinct global positions one swa_fwd call accepts. */
+#define SWA_MAX_GLOBAL 256
+
+/*
+ * swa_fwd: sliding-window attention over whole sequences (prefill / encoder).
+ *
+ *   q, k, v     device, inputs as above (read only)
+ *   out         device, [B, N, Hq, D] of `dtype` (written)
+ *   lse         device, [B, Hq, N] float32 (written); may be NULL to skip it
+ *   B, Hq, Hkv, N, D   sizes; Hq % Hkv == 0
+ *   win_left, win_right >= 0, dilation >= 1.  Windows wider than the sequence
+ *               are clipped, not rejected.
+ *   global_idx  HOST array of n_global positions in [0, N) (may hold
+ *               duplicates, any order); NULL when n_global == 0.  At most
+ *               SWA_MAX_GLOBAL distinct positions.  The array is read during
+ *               the call only.
+ *   scale       multiplier of q.k (1/sqrt(D) for the usual softmax_scale)
+ *   workspace   device scratch of at least swa_fwd_workspace_size(...) bytes,
+ *               caller-owned, contents on entry irrelevant; used only when
+ *               there are global positions (partial results of the global
+ *               query rows, which are split over the keys and merged).  Two
+ *               calls in flight at once must not share it.
+ *
+ * Errors: SWA_ERR_ARG for null q/k/v/out, non-positive sizes, Hq % Hkv != 0,
+ * negative windows, dilation < 1, a global index outside [0, N), n_global < 0
+ * or global_idx NULL with n_global > 0; SWA_ERR_UNSUPPORTED for D not in
+ * {64,128}, an unknown dtype or more than SWA_MAX_GLOBAL distinct globals;
+ * SWA_ERR_WORKSPACE when globals are present and the workspace is NULL or
+ * smaller than swa_fwd_workspace_size(); SWA_ERR_HIP if a launch fails.
+ */
+int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+            int B, int Hq, int Hkv, int N, int D,
+            int win_left, int win_right, int dilation,
+            const int32_t* global_idx, int n_global,
+            float scale, int dtype,
+            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace swa_fwd needs (0 when n_global == 0, in which case
+ * workspace may be NULL).  n_global may count duplicates; 0 on bad sizes. */
+size_t swa_fwd_workspace_size(int B, int Hq, int N, int D, int n_global);
+
+/*
+ * swa_kv_append: write one new token per sequence into the ring (the
+ * RingBuffer append of intelliparadigm.com, section 3.1), on the device:
+ *   kcache[b, :, ring_head[b], :] = k_new[b];  vcache likewise;
+ *   ring_head[b] = (ring_head[b] + 1) % W;  cache_len[b] = min(cache_len[b] + 1, W)
+ *
+ *   kcache, vcache   device, [B, Hkv, W, D] of `dtype` (updated in place)
+ *   k_new, v_new     device, [B, Hkv, D] of `dtype`
+ *   ring_head, cache_len   device int32 [B] (updated in place); on entry
+ *                    0 <= ring_head < W and 0 <= cache_len <= W (not checked
+ *                    on the device: out-of-range values are the caller's error)
+ *
+ * Errors: SWA_ERR_ARG for null pointers or non-positive sizes;
+ * SWA_ERR_UNSUPPORTED for D or dtype; SWA_ERR_HIP if the launch fails.
+ */
+int swa_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new,
+                  int32_t* ring_head, int32_t* cache_len,
+                  int B, int Hkv, int W, int D, int dtype, hipStream_t stream);
+
+/*
+ * swa_decode: one query token per sequence attends over the valid ring slots
+ * (aiqz.cc, "Python demo" and "inference optimisation": the last cache_len
+ * entries, the newest included).  Call it after swa_kv_append for the step.
+ *
+ *   q           device, [B, Hq, D] of `dtype`
+ *   kcache, vcache, ring_head, cache_len   device, as for swa_kv_append (read
+ *               only).  A sequence with cache_len == 0 gets out = 0 and
+ *               lse = -inf.
+ *   out         device, [B, Hq, D] of `dtype`;  lse device [B, Hq] float32
+ *               (may be NULL)
+ *   workspace   device scratch of at least swa_decode_workspace_size(B, Hq, W, D)
+ *               bytes, owned by the caller; its contents on entry do not
+ *               matter.  Two calls in flight at once must not share it.
+ *
+ * Errors: as swa_kv_append, plus SWA_ERR_ARG for Hq % Hkv != 0 and
+ * SWA_ERR_WORKSPACE when the workspace is NULL or too small.
+ */
+int swa_decode(const void* q, const void* kcache, const void* vcache,
+               const int32_t* ring_head, const int32_t* cache_len,
+               void* out, float* lse,
+               int B, int Hq, int Hkv, int W, int D, float scale,
+               void* workspace, size_t workspace_bytes, int dtype, hipStream_t stream);
+
+/* Bytes of device workspace swa_decode needs for these sizes (0 on bad sizes). */
+size_t swa_decode_workspace_size(int B, int Hq, int W, int D);
+
+/* A static, human-readable description of a status code. */
+const char* swa_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int swa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

@@ -1,0 +1,183 @@
+"""ctypes binding of libswa.so (the C ABI in include/swa.h).
+
+Argument marshalling only: shapes are read from the torch tensors, pointers
+and the current HIP stream are passed through, and every step of the
+computation runs in the library's kernels.  There is no fallback: if the
+library has not been built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswa.so")
+
+SWA_F32, SWA_BF16 = 0, 1
+_STATUS = {0: "SWA_OK", -1: "SWA_ERR_ARG", -2: "SWA_ERR_UNSUPPORTED",
+           -3: "SWA_ERR_WORKSPACE", -4: "SWA_ERR_HIP"}
+
+_lib = None
+
+
+class SwaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libswa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SwaError(-4, f"{path} is missing: build it first "
+                           "(python -m sliding_window_attention_tiled_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.swa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, P, I, F, I, P, SZ, P]
+    lib.swa_fwd.restype = I
+    lib.swa_fwd_workspace_size.argtypes = [I, I, I, I, I]
+    lib.swa_fwd_workspace_size.restype = SZ
+    lib.swa_kv_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.swa_kv_append.restype = I
+    lib.swa_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P, SZ, I, P]
+    lib.swa_decode.restype = I
+    lib.swa_decode_workspace_size.argtypes = [I, I, I, I]
+    lib.swa_decode_workspace_size.restype = SZ
+    lib.swa_status_string.argtypes = [I]
+    lib.swa_status_string.restype = ctypes.c_char_p
+    lib.swa_version.argtypes = []
+    lib.swa_version.restype = I
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().swa_status_string(status).decode()
+        raise SwaError(status, f"{what}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SWA_F32
+    if t.dtype == torch.bfloat16:
+        return SWA_BF16
+    raise SwaError(-2, f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor | None, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise SwaError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise SwaError(-1, f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def fwd_workspace_size(B: int, Hq: int, N: int, D: int, n_global: int) -> int:
+    return int(load_library().swa_fwd_workspace_size(B, Hq, N, D, n_global))
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, win_left: int,
+        win_right: int = 0, dilation: int = 1, global_idx=None, scale: float | None = None,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+        workspace: torch.Tensor | None = None, return_lse: bool = True):
+    """Sliding-window attention.  q [B,N,Hq,D], k/v [B,N,Hkv,D] (bf16 or fp32).
+
+    Returns (out [B,N,Hq,D], lse [B,Hq,N] fp32) or out alone when
+    return_lse is False.  scale=None means 1/sqrt(D).  global_idx is a
+    sequence of positions (host side).
+    """
+    lib = load_library()
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, N, Hkv, D) or v.shape != k.shape:
+        raise SwaError(-1, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                           f"v{tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise SwaError(-1, "q, k and v must share one dtype")
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if global_idx is not None and len(global_idx):
+        g = (ctypes.c_int32 * len(global_idx))(*[int(x) for x in global_idx])
+        ng = len(global_idx)
+    else:
+        g, ng = None, 0
+    ws_bytes = 0
+    if ng:
+        need = fwd_workspace_size(B, Hq, N, D, ng)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.swa_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                     _dev(lse, "lse"), B, Hq, Hkv, N, D, win_left, win_right, dilation,
+                     g, ng, float(scale), dt, _dev(workspace, "workspace"), ws_bytes,
+                     _stream(q))
+    _check(st, "swa_fwd")
+    return (out, lse) if return_lse else out
+
+
+def kv_append(kcache: torch.Tensor, vcache: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, ring_head: torch.Tensor, cache_len: torch.Tensor):
+    """In-place ring append.  kcache/vcache [B,Hkv,W,D]; k_new/v_new [B,Hkv,D];
+    ring_head/cache_len int32 [B] on the device."""
+    lib = load_library()
+    B, Hkv, W, D = kcache.shape
+    if vcache.shape != kcache.shape or k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
+        raise SwaError(-1, "kv_append shape mismatch")
+    for t, name in ((ring_head, "ring_head"), (cache_len, "cache_len")):
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise SwaError(-1, f"{name} must be int32 [B]")
+    st = lib.swa_kv_append(_dev(kcache, "kcache"), _dev(vcache, "vcache"),
+                           _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                           _dev(ring_head, "ring_head"), _dev(cache_len, "cache_len"),
+                           B, Hkv, W, D, _dtype_code(kcache), _stream(kcache))
+    _check(st, "swa_kv_append")
+
+
+def decode_workspace_size(B: int, Hq: int, W: int, D: int) -> int:
+    return int(load_library().swa_decode_workspace_size(B, Hq, W, D))
+
+
+def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+           ring_head: torch.Tensor, cache_len: torch.Tensor, *, scale: float | None = None,
+           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+           lse: torch.Tensor | None = None, return_lse: bool = True):
+    """One decode step over the ring.  q [B,Hq,D] -> out [B,Hq,D] (+ lse [B,Hq])."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, W = kcache.shape[1], kcache.shape[2]
+    if kcache.shape != (B, Hkv, W, D) or vcache.shape != kcache.shape:
+        raise SwaError(-1, "decode shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_size(B, Hq, W, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.swa_decode(_dev(q, "q"), _dev(kcache, "kcache"), _dev(vcache, "vcache"),
+                        _dev(ring_head, "ring_head"), _dev(cache_len, "cache_len"),
+                        _dev(out, "out"), _dev(lse, "lse"), B, Hq, Hkv, W, D, float(scale),
+                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                        _dtype_code(q), _stream(q))
+    _check(st, "swa_decode")
+    return (out, lse) if return_lse else out

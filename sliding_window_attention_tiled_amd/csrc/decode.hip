@@ -1,0 +1,427 @@
+// decode.hip -- ring-buffer KV append, split-K decode and the partial combine.
+//
+// The ring (intelliparadigm.com, section 3.1 "cache mechanism": write at
+// idx % size, then advance; aiqz.cc, "inference optimisation": only the last W
+// keys/values are kept) holds W slots per (sequence, kv head), contiguous in
+// memory, so one decode step streams each (b, kv head) slab once.  Decode is
+// bound by that stream (about 4 flop per byte): the slab is split into
+// `splits` slot ranges, one workgroup each, and every wave of a workgroup
+// walks its own 32-slot chunks.  The G query heads of the kv head form the
+// columns of a 16-column MFMA tile, so the K and V of each slot are read once
+// for all heads.  Slots are visited in physical order (keys carry no position,
+// so order does not matter); a slot counts when its age
+// (ring_head - 1 - slot) mod W is below cache_len.  Each workgroup writes one
+// partial (acc, m, l) per head; the combine kernel merges the splits.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "swa_kernels.h"
+
+namespace swa {
+namespace {
+
+// ---- ring append ---------------------------------------------------------------
+// One workgroup per sequence: copy k_new/v_new into slot ring_head[b], then
+// advance ring_head and cache_len once every lane has read the old head.
+__global__ __launch_bounds__(256) void kv_append_kernel(unsigned char* kc, unsigned char* vc,
+                                                        const unsigned char* kn,
+                                                        const unsigned char* vn,
+                                                        int32_t* head, int32_t* len, int Hkv,
+                                                        int W, int row_bytes) {
+    const int b = blockIdx.x;
+    const int slot = head[b];
+    const int chunks = Hkv * row_bytes / 16;  // 16-byte chunks per tensor
+    for (int ci = threadIdx.x; ci < chunks; ci += blockDim.x) {
+        const int h = ci / (row_bytes / 16), c = ci % (row_bytes / 16);
+        const size_t src = ((size_t)b * Hkv + h) * row_bytes + c * 16;
+        const size_t dst = (((size_t)b * Hkv + h) * W + slot) * row_bytes + c * 16;
+        *(u32x4*)(kc + dst) = *(const u32x4*)(kn + src);
+        *(u32x4*)(vc + dst) = *(const u32x4*)(vn + src);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        head[b] = slot + 1 == W ? 0 : slot + 1;
+        len[b] = min(len[b] + 1, W);
+    }
+}
+
+// ---- bf16 split decode on MFMA ----------------------------------------------------
+constexpr int CH = 32;        // slots per chunk
+constexpr int DNT = 256;      // 4 waves
+
+template <int D>
+struct DecCfg {
+    static constexpr int PITCH = D + 8;               // bf16 per LDS row
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int PER_LANE = CH * CPR / 64;    // 16-byte chunks per lane per tensor
+    static constexpr int WAVE_ELEMS = 2 * CH * PITCH; // K and V of one chunk
+};
+
+template <int D>
+__global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams p) {
+    using C = DecCfg<D>;
+    constexpr int KS = D / 32;   // 32-deep k-steps of S^T = K Q^T (16x16x32)
+    constexpr int DB = D / 16;   // 16-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * C::WAVE_ELEMS];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l16 = lane & 15;
+    const int grp = lane >> 4;
+
+    // work item: (b, kv head, head block, split); splits fastest
+    int L = blockIdx.x;
+    const int s = L % p.splits;
+    L /= p.splits;
+    const int hblocks = (p.group + 15) / 16;
+    const int hb = L % hblocks;
+    L /= hblocks;
+    const int kvh = L % p.Hkv;
+    const int b = L / p.Hkv;
+
+    const int head_col = hb * 16 + l16;          // this lane's query head within the group
+    const bool head_ok = head_col < p.group;
+    const int hq = kvh * p.group + head_col;
+
+    const int W = p.W;
+    const int ring_head = p.ring_head[b];
+    const int cache_len = p.cache_len[b];
+    const bool full = cache_len >= W;
+
+    // slots of this wave
+    const int s_lo = s * p.slots_per_split;
+    const int s_hi = min(W, s_lo + p.slots_per_split);
+    const int per_wave = (s_hi - s_lo + 3) / 4;
+    const int w_lo = min(s_hi, s_lo + wave * per_wave);
+    const int w_hi = min(s_hi, w_lo + per_wave);
+    const int n_chunks = (w_hi - w_lo + CH - 1) / CH;
+
+    // Q^T as the B operand: lane holds head column l16, dims ks*32 + grp*8 .. +7
+    bf16x8 qreg[KS];
+    {
+        const __bf16* qp = (const __bf16*)p.q + ((size_t)b * p.Hq + (head_ok ? hq : 0)) * D + grp * 8;
+#pragma unroll
+        for (int k = 0; k < KS; k++)
+            qreg[k] = head_ok ? *(const bf16x8*)(qp + k * 32)
+                              : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+    const size_t slab = ((size_t)b * p.Hkv + kvh) * W;
+    const __bf16* kbase = (const __bf16*)p.kcache + slab * D;
+    const __bf16* vbase = (const __bf16*)p.vcache + slab * D;
+    unsigned short* Ks = smem + wave * C::WAVE_ELEMS;
+    unsigned short* Vs = Ks + CH * C::PITCH;
+
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kEmptyMax, l_run = 0.f;
+    const float c = p.scale_log2;
+
+    u32x4 kr[C::PER_LANE], vr[C::PER_LANE];
+    auto load_chunk = [&](int ck) {
+        const int base = w_lo + ck * CH;
+#pragma unroll
+        for (int u = 0; u < C::PER_LANE; u++) {
+            const int ci = lane + u * 64;
+            const int key = ci / C::CPR, cc = ci % C::CPR;
+            if (base + key < w_hi) {
+                const size_t off = (size_t)(base + key) * D + cc * 8;
+                kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
+                vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
+            } else {
+                kr[u] = u32x4{0u, 0u, 0u, 0u};
+                vr[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    if (n_chunks > 0) load_chunk(0);
+    for (int ck = 0; ck < n_chunks; ck++) {
+        // stage the chunk in this wave's LDS area (natural [slot][d] layout)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < C::PER_LANE; u++) {
+            const int ci = lane + u * 64;
+            const int key = ci / C::CPR, cc = ci % C::CPR;
+            *(u32x4*)(Ks + key * C::PITCH + cc * 8) = kr[u];
+            *(u32x4*)(Vs + key * C::PITCH + cc * 8) = vr[u];
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (ck + 1 < n_chunks) load_chunk(ck + 1);
+
+        // S^T = K Q^T: two 16-slot blocks
+        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int k = 0; k < KS; k++) {
+                const bf16x8 a = *(const bf16x8*)(Ks + (kb * 16 + l16) * C::PITCH + k * 32 + grp * 8);
+                sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[k], sc[kb], 0, 0, 0);
+            }
+        // mask slots beyond the wave range or older than cache_len
+        const int base = w_lo + ck * CH;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int slot = base + kb * 16 + grp * 4 + e;
+                bool valid = slot < w_hi;
+                if (!full) {
+                    int age = ring_head - 1 - slot;
+                    if (age < 0) age += W;
+                    valid = valid && age < cache_len;
+                }
+                if (!valid) sc[kb][e] = -INFINITY;
+            }
+        // online softmax for this lane's head column (lanes l16, l16+16, +32, +48 agree)
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= c;
+        const bool up = mx > m_run + kLazyRescale;
+        const float m_use = up ? mx : m_run;
+        if (__any(up)) {
+            const float alpha = fast_exp2(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+        }
+        m_run = m_use;
+        bf16x8 pb;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const float pe = fast_exp2(__builtin_fmaf(sc[kb][e], c, -m_use));
+                l_run += pe;
+                pb[kb * 4 + e] = (__bf16)pe;
+            }
+        // O^T += V^T P^T: slot (grp*8 + t) of the B operand is key grp*4 + t (t < 4)
+        // or 16 + grp*4 + (t - 4); V^T comes from transposing LDS reads.
+#pragma unroll
+        for (int db = 0; db < DB; db++) {
+            const int col = db * 16 + 4 * (lane & 3);
+            const int key = grp * 4 + (l16 >> 2);
+            const i16x4 lo = lds_read_tr16(Vs + key * C::PITCH + col);
+            const i16x4 hi = lds_read_tr16(Vs + (key + 16) * C::PITCH + col);
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, oacc[db], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the 4 lane groups, then the 4 waves, into one partial per head
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();  // staging areas are free now
+    float* red = (float*)smem;                       // [4 waves][16 heads][D]
+    float* red_ml = red + 4 * 16 * D;                // [4 waves][16 heads][2]
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            red[(wave * 16 + l16) * D + db * 16 + grp * 4 + e] = oacc[db][e];
+    if (grp == 0) {
+        red_ml[(wave * 16 + l16) * 2] = m_run;
+        red_ml[(wave * 16 + l16) * 2 + 1] = l_run;
+    }
+    __syncthreads();
+    const int heads_here = min(16, p.group - hb * 16);
+    for (int idx = threadIdx.x; idx < heads_here * D; idx += DNT) {
+        const int h = idx / D, d = idx % D;
+        float M = kEmptyMax;
+#pragma unroll
+        for (int w = 0; w < 4; w++) M = fmaxf(M, red_ml[(w * 16 + h) * 2]);
+        float acc = 0.f, lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            const float f = fast_exp2(red_ml[(w * 16 + h) * 2] - M);
+            acc += f * red[(w * 16 + h) * D + d];
+            lsum += f * red_ml[(w * 16 + h) * 2 + 1];
+        }
+        const int hq2 = kvh * p.group + hb * 16 + h;
+        float* rec = p.partials + (((size_t)b * p.Hq + hq2) * p.splits + s) * (D + kPartialPad);
+        rec[d] = acc;
+        if (d == 0) {
+            rec[D] = M;
+            rec[D + 1] = lsum;
+        }
+    }
+}
+
+// ---- float32 split decode on the vector ALUs -------------------------------------
+// One wave per (b, query head, split); lanes 16*r .. 16*r+15 share a slot, each
+// lane a D/16 slice of it; four slots per step.
+template <int D>
+__global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
+    constexpr int DL = D / 16;
+    const int lane = threadIdx.x;
+    const int sub = lane >> 4, part = lane & 15;
+    int L = blockIdx.x;
+    const int s = L % p.splits;
+    L /= p.splits;
+    const int hq = L % p.Hq;
+    const int b = L / p.Hq;
+    const int kvh = hq / p.group;
+    const int W = p.W;
+    const int ring_head = p.ring_head[b], cache_len = p.cache_len[b];
+    const int s_lo = s * p.slots_per_split, s_hi = min(W, s_lo + p.slots_per_split);
+
+    float q[DL];
+    const float* qp = (const float*)p.q + ((size_t)b * p.Hq + hq) * D + part * DL;
+#pragma unroll
+    for (int d = 0; d < DL; d++) q[d] = qp[d];
+    const size_t slab = ((size_t)b * p.Hkv + kvh) * W;
+    const float* kbase = (const float*)p.kcache + slab * D + part * DL;
+    const float* vbase = (const float*)p.vcache + slab * D + part * DL;
+    float acc[DL];
+#pragma unroll
+    for (int d = 0; d < DL; d++) acc[d] = 0.f;
+    float m_run = kEmptyMax, l_run = 0.f;
+    const float c = p.scale_log2;
+    for (int base = s_lo; base < s_hi; base += 4) {
+        const int slot = base + sub;
+        bool valid = slot < s_hi;
+        if (valid && cache_len < W) {
+            int age = ring_head - 1 - slot;
+            if (age < 0) age += W;
+            valid = age < cache_len;
+        }
+        float dot = 0.f;
+        if (slot < s_hi) {
+#pragma unroll
+            for (int d = 0; d < DL; d++) dot = __builtin_fmaf(q[d], kbase[(size_t)slot * D + d], dot);
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) dot += __shfl_xor(dot, o);
+        const float sv = valid ? dot * c : -INFINITY;
+        const bool up = sv > m_run + kLazyRescale;
+        const float m_use = up ? sv : m_run;
+        if (up) {
+            const float alpha = fast_exp2(m_run - m_use);
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < DL; d++) acc[d] *= alpha;
+        }
+        m_run = m_use;
+        const float pk = fast_exp2(sv - m_use);
+        l_run += pk;
+        if (valid) {
+#pragma unroll
+            for (int d = 0; d < DL; d++) acc[d] = __builtin_fmaf(pk, vbase[(size_t)slot * D + d], acc[d]);
+        }
+    }
+    // merge the four slot lanes (sub = 0..3) of each dim slice
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        const float m_o = __shfl_xor(m_run, o);
+        const float l_o = __shfl_xor(l_run, o);
+        const float M = fmaxf(m_run, m_o);
+        const float fa = fast_exp2(m_run - M), fb = fast_exp2(m_o - M);
+#pragma unroll
+        for (int d = 0; d < DL; d++) {
+            const float a_o = __shfl_xor(acc[d], o);
+            acc[d] = acc[d] * fa + a_o * fb;
+        }
+        l_run = l_run * fa + l_o * fb;
+        m_run = M;
+    }
+    if (sub == 0) {
+        float* rec = p.partials + (((size_t)b * p.Hq + hq) * p.splits + s) * (D + kPartialPad);
+#pragma unroll
+        for (int d = 0; d < DL; d++) rec[part * DL + d] = acc[d];
+        if (part == 0) {
+            rec[D] = m_run;
+            rec[D + 1] = l_run;
+        }
+    }
+}
+
+// ---- merge split partials ------------------------------------------------------------
+// One wave per output row: M = max m_s, L = sum l_s 2^(m_s - M),
+// out = sum acc_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  A row with no keys
+// (L == 0) gets out = 0 and lse = -inf.
+template <int D, typename OutT>
+__global__ __launch_bounds__(64) void combine_kernel(const CombineParams p) {
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float* rec0 = p.partials + (size_t)row * p.splits * (D + kPartialPad);
+    float M = kEmptyMax;
+    for (int s = 0; s < p.splits; s++) M = fmaxf(M, rec0[s * (D + kPartialPad) + D]);
+    float L = 0.f;
+    float acc[D / 64];
+#pragma unroll
+    for (int i = 0; i < D / 64; i++) acc[i] = 0.f;
+    for (int s = 0; s < p.splits; s++) {
+        const float* rec = rec0 + s * (D + kPartialPad);
+        const float f = fast_exp2(rec[D] - M);
+        L += f * rec[D + 1];
+#pragma unroll
+        for (int i = 0; i < D / 64; i++) acc[i] += f * rec[lane + i * 64];
+    }
+    size_t out_off, lse_off;
+    if (p.mode == 0) {
+        out_off = (size_t)row * D;
+        lse_off = row;
+    } else {
+        const int gi = row % p.n_global;
+        const int bh = row / p.n_global;  // b * Hq + h
+        const int b = bh / p.Hq, h = bh % p.Hq;
+        const int pos = p.gpos[gi];
+        out_off = (((size_t)b * p.N + pos) * p.Hq + h) * D;
+        lse_off = (size_t)bh * p.N + pos;
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    OutT* op = (OutT*)p.out + out_off;
+#pragma unroll
+    for (int i = 0; i < D / 64; i++) op[lane + i * 64] = (OutT)(acc[i] * inv);
+    if (p.lse != nullptr && lane == 0)
+        p.lse[lse_off] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn, int32_t* head,
+                            int32_t* len, int B, int Hkv, int W, int D, int elem_bytes,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(kv_append_kernel, dim3(B), dim3(256), 0, s, (unsigned char*)kc,
+                       (unsigned char*)vc, (const unsigned char*)kn, (const unsigned char*)vn,
+                       head, len, Hkv, W, D * elem_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, hipStream_t s) {
+    const int grid = p.B * p.Hkv * ((p.group + 15) / 16) * p.splits;
+    if (D == 128)
+        hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3(grid), dim3(DNT), 0, s, p);
+    else
+        hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(grid), dim3(DNT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_f32(const DecodeParams& p, int D, hipStream_t s) {
+    const int grid = p.B * p.Hq * p.splits;
+    if (D == 128)
+        hipLaunchKernelGGL(decode_f32_kernel<128>, dim3(grid), dim3(64), 0, s, p);
+    else
+        hipLaunchKernelGGL(decode_f32_kernel<64>, dim3(grid), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t s) {
+    if (p.rows == 0) return hipSuccess;
+    if (dtype == SWA_BF16) {
+        if (D == 128)
+            hipLaunchKernelGGL((combine_kernel<128, __bf16>), dim3(p.rows), dim3(64), 0, s, p);
+        else
+            hipLaunchKernelGGL((combine_kernel<64, __bf16>), dim3(p.rows), dim3(64), 0, s, p);
+    } else {
+        if (D == 128)
+            hipLaunchKernelGGL((combine_kernel<128, float>), dim3(p.rows), dim3(64), 0, s, p);
+        else
+            hipLaunchKernelGGL((combine_kernel<64, float>), dim3(p.rows), dim3(64), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace swa

@@ -1,0 +1,219 @@
+// swa_api.cpp -- the C ABI of libswa.so (declared in include/swa.h): argument
+// validation, normalisation of the global set, work planning and launches.
+// Nothing here allocates device memory or synchronises the host.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "swa_kernels.h"
+
+namespace {
+
+using swa::CombineParams;
+using swa::DecodeParams;
+using swa::FwdParams;
+
+constexpr int kMaxN = 1 << 30;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool supported_d(int D) { return D == 64 || D == 128; }
+bool known_dtype(int dt) { return dt == SWA_F32 || dt == SWA_BF16; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Key chunking of global query rows: at most 32 chunks, each a multiple of 64 keys.
+void global_chunks(int N, int* chunk, int* nchunks) {
+    int64_t nc = std::min<int64_t>(32, std::max<int64_t>(1, cdiv(N, 512)));
+    int64_t ck = cdiv(cdiv(N, nc), 64) * 64;
+    *chunk = (int)ck;
+    *nchunks = (int)cdiv(N, ck);
+}
+
+// Splits of a decode ring: enough workgroups to cover the GPU several times
+// over, each split a multiple of 128 slots.
+void decode_splits(int B, int Hq, int W, int* splits, int* per_split) {
+    const int64_t rows = (int64_t)B * Hq;
+    int64_t sp = std::max<int64_t>(1, cdiv(8192, rows));
+    sp = std::min<int64_t>(sp, std::max<int64_t>(1, W / 128));
+    int64_t ps = cdiv(cdiv(W, sp), 128) * 128;
+    *per_split = (int)ps;
+    *splits = (int)cdiv(W, ps);
+}
+
+int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+
+}  // namespace
+
+extern "C" {
+
+const char* swa_status_string(int status) {
+    switch (status) {
+        case SWA_OK: return "success";
+        case SWA_ERR_ARG: return "invalid argument";
+        case SWA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or global count";
+        case SWA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SWA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int swa_version(void) { return 100; }
+
+size_t swa_fwd_workspace_size(int B, int Hq, int N, int D, int n_global) {
+    if (B <= 0 || Hq <= 0 || N <= 0 || N > kMaxN || !supported_d(D) || n_global < 0) return 0;
+    if (n_global == 0) return 0;
+    const int ng = std::min(n_global, SWA_MAX_GLOBAL);
+    int chunk, nchunks;
+    global_chunks(N, &chunk, &nchunks);
+    return (size_t)B * Hq * ng * nchunks * swa::partial_floats(D) * sizeof(float);
+}
+
+int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+            int Hkv, int N, int D, int win_left, int win_right, int dilation,
+            const int32_t* global_idx, int n_global, float scale, int dtype, void* workspace,
+            size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !out) return SWA_ERR_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || N > kMaxN || D <= 0) return SWA_ERR_ARG;
+    if (Hq % Hkv != 0) return SWA_ERR_ARG;
+    if (win_left < 0 || win_right < 0 || dilation < 1) return SWA_ERR_ARG;
+    if (n_global < 0 || (n_global > 0 && !global_idx)) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+
+    std::vector<int32_t> g;
+    if (n_global > 0) {
+        g.assign(global_idx, global_idx + n_global);
+        for (int32_t x : g)
+            if (x < 0 || x >= N) return SWA_ERR_ARG;
+        std::sort(g.begin(), g.end());
+        g.erase(std::unique(g.begin(), g.end()), g.end());
+        if ((int)g.size() > SWA_MAX_GLOBAL) return SWA_ERR_UNSUPPORTED;
+        if (!workspace || workspace_bytes < swa_fwd_workspace_size(B, Hq, N, D, (int)g.size()))
+            return SWA_ERR_WORKSPACE;
+    }
+
+    FwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.partials = (float*)workspace;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = N;
+    p.group = Hq / Hkv;
+    p.causal = win_right == 0;
+    p.wl = std::min(win_left, N);   // wider windows change nothing
+    p.wr = std::min(win_right, N);
+    p.dil = dilation;
+    p.scale_log2 = scale * kLog2e;
+    p.qd = N / dilation;
+    p.rem = N % dilation;
+    if (dtype == SWA_BF16) {
+        p.hpw = gcd(p.group, 4);
+        p.bmq = (4 / p.hpw) * 32;
+    } else {
+        p.hpw = 1;
+        p.bmq = 64;
+    }
+    p.head_groups = p.group / p.hpw;
+    p.tiles_long = (int)cdiv(p.qd + 1, p.bmq);
+    p.tiles_short = (int)cdiv(p.qd, p.bmq);
+    const int64_t per_slab =
+        (int64_t)p.rem * p.tiles_long + (int64_t)(dilation - p.rem) * p.tiles_short;
+    const int64_t blocks = (int64_t)B * Hkv * p.head_groups * per_slab;
+    if (per_slab > INT32_MAX || blocks > INT32_MAX) return SWA_ERR_ARG;
+    p.tiles_per_slab = (int)per_slab;
+    p.n_blocks = (int)blocks;
+
+    p.n_global = (int)g.size();
+    for (int i = 0; i < p.n_global; i++) p.gpos[i] = g[i];
+    global_chunks(N, &p.g_chunk, &p.g_nchunks);
+    const int rows_wg = dtype == SWA_BF16 ? (4 / p.hpw) * 32 : 64;
+    p.g_rowgroups = (int)cdiv(p.n_global, rows_wg);
+
+    hipError_t e = dtype == SWA_BF16 ? swa::launch_fwd_bf16(p, D, stream)
+                                     : swa::launch_fwd_f32(p, D, stream);
+    if (e != hipSuccess) return SWA_ERR_HIP;
+    if (p.n_global > 0) {
+        CombineParams c;
+        std::memset(&c, 0, sizeof c);
+        c.partials = p.partials;
+        c.out = out;
+        c.lse = lse;
+        c.rows = B * Hq * p.n_global;
+        c.splits = p.g_nchunks;
+        c.mode = 1;
+        c.B = B;
+        c.Hq = Hq;
+        c.N = N;
+        c.n_global = p.n_global;
+        std::memcpy(c.gpos, p.gpos, sizeof c.gpos);
+        if (swa::launch_combine(c, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
+    }
+    return SWA_OK;
+}
+
+int swa_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new,
+                  int32_t* ring_head, int32_t* cache_len, int B, int Hkv, int W, int D,
+                  int dtype, hipStream_t stream) {
+    if (!kcache || !vcache || !k_new || !v_new || !ring_head || !cache_len) return SWA_ERR_ARG;
+    if (B <= 0 || Hkv <= 0 || W <= 0 || D <= 0) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    const int elem = dtype == SWA_BF16 ? 2 : 4;
+    hipError_t e = swa::launch_kv_append(kcache, vcache, k_new, v_new, ring_head, cache_len, B,
+                                         Hkv, W, D, elem, stream);
+    return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+}
+
+size_t swa_decode_workspace_size(int B, int Hq, int W, int D) {
+    if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(D)) return 0;
+    int splits, per;
+    decode_splits(B, Hq, W, &splits, &per);
+    return (size_t)B * Hq * splits * swa::partial_floats(D) * sizeof(float);
+}
+
+int swa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ring_head,
+               const int32_t* cache_len, void* out, float* lse, int B, int Hq, int Hkv, int W,
+               int D, float scale, void* workspace, size_t workspace_bytes, int dtype,
+               hipStream_t stream) {
+    if (!q || !kcache || !vcache || !ring_head || !cache_len || !out) return SWA_ERR_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0 || D <= 0 || Hq % Hkv != 0) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < swa_decode_workspace_size(B, Hq, W, D))
+        return SWA_ERR_WORKSPACE;
+    DecodeParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.kcache = kcache;
+    p.vcache = vcache;
+    p.ring_head = ring_head;
+    p.cache_len = cache_len;
+    p.partials = (float*)workspace;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.W = W;
+    p.group = Hq / Hkv;
+    p.scale_log2 = scale * kLog2e;
+    decode_splits(B, Hq, W, &p.splits, &p.slots_per_split);
+    hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, stream)
+                                     : swa::launch_decode_f32(p, D, stream);
+    if (e != hipSuccess) return SWA_ERR_HIP;
+    CombineParams c;
+    std::memset(&c, 0, sizeof c);
+    c.partials = p.partials;
+    c.out = out;
+    c.lse = lse;
+    c.rows = B * Hq;
+    c.splits = p.splits;
+    c.mode = 0;
+    c.B = B;
+    c.Hq = Hq;
+    if (swa::launch_combine(c, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
+    return SWA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// swa_kernels.h -- parameter blocks shared by the host API (swa_api.cpp) and
+// the HIP kernels of libswa.so.  Internal to the library.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/swa.h"
+
+namespace swa {
+
+// Partial softmax state written by split-K passes and merged by the combine
+// kernel: acc[D] (unnormalised weighted sum of v), m (running max of the
+// scaled scores, base-2 units), l (sum of 2^(s - m)).  Records are padded to
+// a multiple of 16 bytes.
+constexpr int kPartialPad = 4;
+inline int partial_floats(int D) { return D + kPartialPad; }
+
+// Upper bound of score contributions kept without rescaling: the running max
+// is only moved when a tile's max exceeds it by more than this (base-2 units),
+// so unnormalised weights stay <= 2^kLazyRescale.
+constexpr float kLazyRescale = 8.0f;
+
+// One forward launch.  Positions are split into residue classes r = i mod d;
+// inside a class the dilated window is an ordinary window over m = (i - r) / d.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;        // may be null
+    float* partials;   // global-row partials [B][Hq][n_global][g_nchunks][D+4]
+    int B, Hq, Hkv, N, group;   // group = Hq / Hkv
+    int wl, wr, dil, causal;
+    float scale_log2;  // scale * log2(e)
+    // residue classes: N = qd * dil + rem; classes r < rem hold qd + 1 positions
+    int qd, rem;
+    // band work decomposition
+    int hpw;           // query heads per workgroup (1, 2 or 4)
+    int bmq;           // query positions per workgroup (per residue class)
+    int tiles_long, tiles_short;  // position tiles in a long / short residue class
+    int tiles_per_slab;           // all tiles of one (b, kv head, head group)
+    int head_groups;              // group / hpw
+    int n_blocks;                 // grid size of the band launch
+    // global tokens (sorted, unique)
+    int n_global;
+    int g_chunk;       // keys per split of a global row
+    int g_nchunks;     // splits per global row
+    int g_rowgroups;   // workgroups needed to cover n_global rows
+    int32_t gpos[SWA_MAX_GLOBAL];
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* kcache;
+    const void* vcache;
+    const int32_t* ring_head;
+    const int32_t* cache_len;
+    float* partials;   // [B][Hq][splits][D+4]
+    int B, Hq, Hkv, W, group;
+    int splits;        // workgroups per (b, kv head)
+    int slots_per_split;
+    float scale_log2;
+};
+
+struct CombineParams {
+    const float* partials;  // [rows][splits][D+4]
+    void* out;
+    float* lse;             // may be null
+    int rows, splits;
+    int mode;               // 0: decode rows (b*Hq + h); 1: global rows of a forward
+    int B, Hq, N, n_global;
+    const int32_t* gpos_dev;  // unused (global positions come in gpos below)
+    int32_t gpos[SWA_MAX_GLOBAL];
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
+hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn,
+                            int32_t* head, int32_t* len, int B, int Hkv, int W, int D,
+                            int elem_bytes, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams& p, int D, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t s);
+
+}  // namespace swa

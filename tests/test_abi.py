@@ -1,0 +1,135 @@
+"""The C-ABI library: it loads, exports every declared entry point, and rejects
+bad arguments before anything is enqueued.  No GPU is needed: every call here
+fails validation, so no HIP runtime call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_attention_tiled_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+OK, ARG, UNSUP, WS = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libswa.so is not built (python -m sliding_window_attention_tiled_amd.build)")
+    return binding.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_\w+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ["swa_fwd", "swa_fwd_workspace_size", "swa_kv_append", "swa_decode",
+              "swa_decode_workspace_size", "swa_status_string", "swa_version"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in swa.h but not exported"
+
+
+def test_status_strings(lib):
+    for st in (OK, ARG, UNSUP, WS, -4):
+        assert lib.swa_status_string(st)
+    assert lib.swa_status_string(12345) == b"unknown status"
+    assert lib.swa_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    assert lib.swa_fwd_workspace_size(1, 8, 1024, 128, 0) == 0
+    a = lib.swa_fwd_workspace_size(2, 8, 8192, 64, 16)
+    assert a > 0 and a % 16 == 0
+    assert lib.swa_fwd_workspace_size(2, 8, 8192, 64, 32) == 2 * a
+    assert lib.swa_fwd_workspace_size(2, 8, 8192, 96, 16) == 0      # unsupported D
+    assert lib.swa_decode_workspace_size(64, 32, 4096, 128) > 0
+    assert lib.swa_decode_workspace_size(0, 32, 4096, 128) == 0
+    assert lib.swa_decode_workspace_size(1, 1, 1, 64) > 0
+
+
+P = ctypes.c_void_p(256)  # stands in for a device pointer; never dereferenced
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, out=P, lse=None, B=1, Hq=4, Hkv=2, N=128, D=128, wl=7, wr=0,
+             dil=1, g=None, ng=0, scale=0.1, dtype=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.swa_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                       a["N"], a["D"], a["wl"], a["wr"], a["dil"], a["g"], a["ng"],
+                       a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ARG), (dict(k=None), ARG), (dict(v=None), ARG), (dict(out=None), ARG),
+    (dict(B=0), ARG), (dict(N=0), ARG), (dict(Hq=0), ARG), (dict(Hkv=0), ARG),
+    (dict(Hq=6, Hkv=4), ARG), (dict(wl=-1), ARG), (dict(wr=-2), ARG), (dict(dil=0), ARG),
+    (dict(ng=-1), ARG), (dict(ng=3), ARG),                       # NULL global_idx
+    (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(dtype=7), UNSUP),
+])
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_fwd_global_validation(lib):
+    g = (ctypes.c_int32 * 3)(0, 5, 128)                           # 128 is out of range
+    assert fwd(lib, g=g, ng=3) == ARG
+    g = (ctypes.c_int32 * 3)(0, 5, -1)
+    assert fwd(lib, g=g, ng=3) == ARG
+    g = (ctypes.c_int32 * 3)(0, 5, 9)
+    assert fwd(lib, g=g, ng=3) == WS                             # no workspace
+    need = lib.swa_fwd_workspace_size(1, 4, 128, 128, 3)
+    assert fwd(lib, g=g, ng=3, ws=P, wsb=need - 1) == WS         # too small
+    big = (ctypes.c_int32 * 300)(*range(300))
+    assert fwd(lib, N=1000, g=big, ng=300) == UNSUP              # > 256 distinct
+    dup = (ctypes.c_int32 * 300)(*([3] * 300))                   # duplicates collapse
+    assert fwd(lib, N=1000, g=dup, ng=300) == WS
+
+
+def test_kv_append_validation(lib):
+    f = lib.swa_kv_append
+    assert f(None, P, P, P, P, P, 1, 1, 8, 128, 1, None) == ARG
+    assert f(P, P, P, P, None, P, 1, 1, 8, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 0, 1, 8, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 1, 1, 0, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 1, 1, 8, 100, 1, None) == UNSUP
+    assert f(P, P, P, P, P, P, 1, 1, 8, 128, 5, None) == UNSUP
+
+
+def test_decode_validation(lib):
+    f = lib.swa_decode
+    need = lib.swa_decode_workspace_size(2, 8, 64, 128)
+    base = [P, P, P, P, P, P, None, 2, 8, 2, 64, 128, 0.1, P, need, 1, None]
+    def call(**ch):
+        a = list(base)
+        names = ["q", "kc", "vc", "head", "len", "out", "lse", "B", "Hq", "Hkv", "W", "D",
+                 "scale", "ws", "wsb", "dtype", "stream"]
+        for k_, v_ in ch.items():
+            a[names.index(k_)] = v_
+        return f(*a)
+    assert call(q=None) == ARG
+    assert call(head=None) == ARG
+    assert call(out=None) == ARG
+    assert call(Hq=6, Hkv=4) == ARG
+    assert call(W=0) == ARG
+    assert call(D=80) == UNSUP
+    assert call(dtype=3) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=need - 4) == WS
+
+
+def test_python_binding_requires_device_tensors(lib):
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(binding.SwaError):
+        binding.fwd(q, q, q, win_left=3)
