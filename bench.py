@@ -44,7 +44,25 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--cpu-rows", type=int, default=32768)
+    ap.add_argument("--only", choices=["fwd", "decode"], default=None,
+                    help="run one leg only (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy, the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(reps: int = 3):
+    """A plain copy of 2^30 bytes, repeated: the counter reading of one dispatch
+    divided by 2^20 KiB read (and written) gives the scale factor of the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "reps": reps}))
 
 
 def to_dev(x):
@@ -174,6 +192,12 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.only == "decode":
+        print(json.dumps({"decode": bench_decode(args)}))
+        return
     f = bench_fwd(args)
     ms = f["ms_kernel"]
     value = f["nominal_flop"] / (ms * 1e-3) / 1e12
@@ -199,9 +223,9 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(exact_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
-    if not args.no_decode:
+    if not args.no_decode and args.only is None:
         res["decode"] = bench_decode(args)
-    if not args.no_cpu:
+    if not args.no_cpu and args.only is None:
         res["cpu_baseline"] = cpu_baseline(f["inputs"], f["cfg"], args.cpu_rows)
     print(json.dumps(res))
 

@@ -17,7 +17,9 @@
 // probabilities are rounded to bf16 and multiplied with V^T, read from the
 // natural-layout V tile through ds_read_b64_tr_b16.  The softmax is kept
 // online (running max m, sum l, rescaled accumulator), with the max moved only
-// when a tile exceeds it by more than 2^8, which is exact up to rounding.
+// when a tile exceeds it by more than 2^8, which is exact up to rounding; the
+// running sum adds the bf16-rounded weights, the same ones the products with
+// V use, so out is normalised by exactly the weights it was built from.
 //
 // Global tokens (aiqz.cc "Sliding window attention: Mistral", section
 // "global attention tokens"): after the band, a band workgroup also visits
@@ -32,35 +34,79 @@
 #include "fwd_common.h"
 #include "swa_kernels.h"
 
+// LDS row pitches (bf16 elements).  K rows are read 16 B per lane, 16 rows per
+// LDS cycle: a pitch of 4 (mod 64) dwords puts those rows on distinct banks.
+// V rows are read by ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes: a pitch
+// of 16 (mod 64) dwords keeps those on distinct banks.
+#ifndef SWA_FWD_KPAD
+#define SWA_FWD_KPAD 8
+#endif
+
 namespace swa {
 namespace {
 
 constexpr int BN = 64;        // keys per K/V tile
 constexpr int NTHREADS = 256; // 4 waves
+constexpr int kFarAway = -(1 << 30);  // residue coordinate outside every window
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct TileCfg {
-    static constexpr int PITCH = D + 8;               // bf16 elements per LDS row
-    static constexpr int ELEMS = BN * PITCH;          // one K or V tile
-    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int KP = D + SWA_FWD_KPAD;                 // K row pitch
+#ifdef SWA_FWD_VPAD
+    static constexpr int VP = D + SWA_FWD_VPAD;
+#else
+    static constexpr int VP = ((D + 95) / 128) * 128 + 32;       // = 32 (mod 128)
+#endif
+    static constexpr int K_ELEMS = BN * KP;
+    static constexpr int V_ELEMS = BN * VP;
+    static constexpr int STAGE = K_ELEMS + V_ELEMS;
+    static constexpr int CPR = D / 8;                            // 16-byte chunks per row
     static constexpr int PER_THREAD = BN * CPR / NTHREADS;
+    static constexpr int KEY_STEP = NTHREADS / CPR;              // rows between a thread's chunks
     static_assert(PER_THREAD * NTHREADS == BN * CPR, "tile does not split evenly");
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile_regs(u32x4 (&kr)[TileCfg<D>::PER_THREAD],
-                                               u32x4 (&vr)[TileCfg<D>::PER_THREAD],
-                                               const __bf16* kbase, const __bf16* vbase,
-                                               int rowstride, const KeyStream& ks,
-                                               const FwdParams& p, int j, bool grows) {
+// Loads tile j of the key stream into registers (zero rows for padding).
+// For gathered global-key tiles it also records, per key, the position and
+// the residue coordinate g / d when g is in this residue class (else a value
+// no window reaches) in gk[2][BN], for the element masks.
+template <int D, bool GROWS>
+__device__ __forceinline__ void load_tile(u32x4 (&kr)[TileCfg<D>::PER_THREAD],
+                                          u32x4 (&vr)[TileCfg<D>::PER_THREAD],
+                                          const __bf16* kbase, const __bf16* vbase,
+                                          int rowstride, const KeyStream& ks, const FwdParams& p,
+                                          int j, int* gk) {
     using T = TileCfg<D>;
+    const int key0 = threadIdx.x / T::CPR;
+    const int c = threadIdx.x % T::CPR;
+    int kpos[T::PER_THREAD];
+    if (GROWS || j < ks.n_band_tiles) {
+        const int kk0 = ks.k_lo + j * BN + key0;
+#pragma unroll
+        for (int u = 0; u < T::PER_THREAD; u++) {
+            const int kk = kk0 + u * T::KEY_STEP;
+            kpos[u] = kk <= ks.k_hi ? ks.r + kk * ks.dil : -1;
+        }
+    } else {
+        const int g0 = (j - ks.n_band_tiles) * BN + key0;
+#pragma unroll
+        for (int u = 0; u < T::PER_THREAD; u++) {
+            const int gi = g0 + u * T::KEY_STEP;
+            kpos[u] = gi < ks.n_global ? p.gpos[gi] : -1;
+            if (c == 0) {
+                const int g = kpos[u];
+                gk[key0 + u * T::KEY_STEP] = g;
+                gk[BN + key0 + u * T::KEY_STEP] =
+                    (g >= 0 && g % ks.dil == ks.r) ? g / ks.dil : kFarAway;
+            }
+        }
+    }
 #pragma unroll
     for (int u = 0; u < T::PER_THREAD; u++) {
-        const int ci = threadIdx.x + u * NTHREADS;
-        const int key = ci / T::CPR, c = ci % T::CPR;
-        const int pos = key_position(ks, p, j, key, BN, grows);
-        if (pos >= 0) {
-            const size_t off = (size_t)pos * rowstride + c * 8;
+        if (kpos[u] >= 0) {
+            const size_t off = (size_t)kpos[u] * rowstride + c * 8;
             kr[u] = *(const u32x4*)(kbase + off);
             vr[u] = *(const u32x4*)(vbase + off);
         } else {
@@ -71,16 +117,17 @@ __device__ __forceinline__ void load_tile_regs(u32x4 (&kr)[TileCfg<D>::PER_THREA
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile_lds(const u32x4 (&kr)[TileCfg<D>::PER_THREAD],
-                                               const u32x4 (&vr)[TileCfg<D>::PER_THREAD],
-                                               unsigned short* ks_lds, unsigned short* vs_lds) {
+__device__ __forceinline__ void store_tile(const u32x4 (&kr)[TileCfg<D>::PER_THREAD],
+                                           const u32x4 (&vr)[TileCfg<D>::PER_THREAD],
+                                           unsigned short* stage) {
     using T = TileCfg<D>;
+    const int key0 = threadIdx.x / T::CPR;
+    const int c = threadIdx.x % T::CPR;
 #pragma unroll
     for (int u = 0; u < T::PER_THREAD; u++) {
-        const int ci = threadIdx.x + u * NTHREADS;
-        const int key = ci / T::CPR, c = ci % T::CPR;
-        *(u32x4*)(ks_lds + key * T::PITCH + c * 8) = kr[u];
-        *(u32x4*)(vs_lds + key * T::PITCH + c * 8) = vr[u];
+        const int key = key0 + u * T::KEY_STEP;
+        *(u32x4*)(stage + key * T::KP + c * 8) = kr[u];
+        *(u32x4*)(stage + T::K_ELEMS + key * T::VP + c * 8) = vr[u];
     }
 }
 
@@ -93,10 +140,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     constexpr int KC = D / 16;   // 16-deep k-steps of QK^T
     constexpr int DB = D / 32;   // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * T::ELEMS];
-    // stage st: K tile at smem + 2*st*ELEMS, V tile right after it
-    auto k_lds = [&](int st) { return smem + 2 * st * T::ELEMS; };
-    auto v_lds = [&](int st) { return smem + (2 * st + 1) * T::ELEMS; };
+    __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) int gk_lds[2][2 * BN];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -108,7 +153,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                               : decode_band_item(p, xcd_contiguous(blockIdx.x, gridDim.x), BN);
     const int b = wi.b, kvh = wi.kvh, hg = wi.hg, chunk = wi.chunk;
     const KeyStream& ks = wi.ks;
-    // wave_row0: residue coordinate (band) or global index (GROWS) of the wave's first row
+    // residue coordinate (band) or global index (GROWS) of the wave's first row
     const int wave_row0 = wi.row0 + (wave / p.hpw) * 32 * QB;
     const int hq = kvh * p.group + hg * p.hpw + (wave % p.hpw);
 
@@ -133,17 +178,12 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         const __bf16* qp = (const __bf16*)p.q +
                            (((size_t)b * p.N + max(qpos[qb], 0)) * p.Hq + hq) * D + half * 8;
 #pragma unroll
-        for (int kc = 0; kc < KC; kc++) {
-            if (qpos[qb] >= 0) {
-                qreg[qb][kc] = *(const bf16x8*)(qp + kc * 16);
-            } else {
-                qreg[qb][kc] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-            }
-        }
+        for (int kc = 0; kc < KC; kc++)
+            qreg[qb][kc] = qpos[qb] >= 0 ? *(const bf16x8*)(qp + kc * 16)
+                                         : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    // wave row range in residue coordinates (band) for tile classification
     const int w_first = wave_row0;
-    const int w_last_raw = wave_row0 + 32 * QB - 1;
+    const int w_last = min(wave_row0 + 32 * QB - 1, ks.Nr - 1);
 
     f32x16 oacc[QB][DB];
     float m_run[QB], l_run[QB];
@@ -155,33 +195,35 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         for (int db = 0; db < DB; db++) oacc[qb][db] = f32x16{};
     }
     const float c = p.scale_log2;
+    const __bf16 one = (__bf16)1.0f;
+    const bf16x2 ones = {one, one};
 
     // ---- prologue: tile 0 into stage 0 ---------------------------------------
     u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
     if (ks.n_tiles > 0) {
-        load_tile_regs<D>(kr, vr, kbase, vbase, rowstride, ks, p, 0, GROWS);
-        store_tile_lds<D>(kr, vr, k_lds(0), v_lds(0));
+        load_tile<D, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, 0, gk_lds[0]);
+        store_tile<D>(kr, vr, smem);
     }
     __syncthreads();
 
     for (int j = 0; j < ks.n_tiles; j++) {
         const int st = j & 1;
         const bool has_next = j + 1 < ks.n_tiles;
-        if (has_next) load_tile_regs<D>(kr, vr, kbase, vbase, rowstride, ks, p, j + 1, GROWS);
+        if (has_next)
+            load_tile<D, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, j + 1, gk_lds[st ^ 1]);
 
         // classify this tile for this wave (wave-uniform)
         const bool band_tile = GROWS || j < ks.n_band_tiles;
+        const int kt0 = ks.k_lo + j * BN;
         bool skip = false, need_mask = true;
         if (!GROWS && band_tile) {
-            const int kt0 = ks.k_lo + j * BN;
             const int kt1 = kt0 + BN - 1;
-            const int w_last = min(w_last_raw, ks.Nr - 1);
             skip = w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl;
             need_mask = !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
         }
         if (!skip) {
-            const unsigned short* Ks = k_lds(st);
-            const unsigned short* Vs = v_lds(st);
+            const unsigned short* Ks = smem + st * T::STAGE;
+            const unsigned short* Vs = Ks + T::K_ELEMS;
             // S^T = K Q^T : two 32-key blocks x QB 32-query blocks
             f32x16 s[QB][2];
 #pragma unroll
@@ -194,42 +236,75 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
                 for (int kb = 0; kb < 2; kb++) {
                     const bf16x8 a =
-                        *(const bf16x8*)(Ks + (kb * 32 + l32) * T::PITCH + kc * 16 + half * 8);
+                        *(const bf16x8*)(Ks + (kb * 32 + l32) * T::KP + kc * 16 + half * 8);
 #pragma unroll
                     for (int qb = 0; qb < QB; qb++)
                         s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][kc],
                                                                             s[qb][kb], 0, 0, 0);
                 }
             }
-            // element masks (edge tiles, global-key tiles, GROWS tiles)
+            // Element masks.  Lane key offsets within the tile are
+            // kb*32 + (e>>2)*8 + half*4 + (e&3); all compares are per element.
             if (need_mask) {
+                if (GROWS) {
 #pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
+                    for (int qb = 0; qb < QB; qb++) {
+                        const int hi = p.causal ? min(ks.k_hi, qpos[qb]) : ks.k_hi;
+                        const int lim = hi - kt0 - half * 4;  // valid when offset <= lim
 #pragma unroll
-                    for (int e = 0; e < 16; e++) {
-                        const int koff = kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                        for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-                        for (int qb = 0; qb < QB; qb++) {
-                            bool valid;
-                            if (GROWS) {
-                                const int kk = ks.k_lo + j * BN + koff;
-                                valid = kk <= ks.k_hi && qpos[qb] >= 0 &&
-                                        (!p.causal || kk <= qpos[qb]);
-                            } else if (band_tile) {
-                                const int kk = ks.k_lo + j * BN + koff;
-                                const int dl = kk - qres[qb];
-                                valid = kk <= ks.k_hi && dl >= -p.wl && dl <= p.wr;
-                            } else {
-                                const int gi = (j - ks.n_band_tiles) * BN + koff;
-                                valid = gi < ks.n_global && qpos[qb] >= 0 &&
-                                        global_key_visible(p, ks, p.gpos[gi], qres[qb], qpos[qb]);
+                            for (int e = 0; e < 16; e++) {
+                                const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
+                                if (ko > lim) s[qb][kb][e] = -INFINITY;
                             }
-                            if (!valid) s[qb][kb][e] = -INFINITY;
-                        }
                     }
+                } else if (band_tile) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; qb++) {
+                        // dl = key - query; valid when -wl <= dl <= wr and key <= k_hi
+                        const int base = kt0 + half * 4 - qres[qb] + p.wl;
+                        const unsigned span = (unsigned)(p.wl + p.wr);
+                        const int lim = ks.k_hi - kt0 - half * 4;
+#pragma unroll
+                        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                            for (int e = 0; e < 16; e++) {
+                                const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
+                                const bool ok = (unsigned)(base + ko) <= span && ko <= lim;
+                                if (!ok) s[qb][kb][e] = -INFINITY;
+                            }
+                    }
+                } else {
+                    // gathered global keys: visible unless already in the band,
+                    // and (causal) not after the query
+                    const int* gk = gk_lds[st];
+                    const unsigned span = (unsigned)(p.wl + p.wr);
+#pragma unroll
+                    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; e4++) {
+                            const int4 g4 = *(const int4*)(gk + kb * 32 + e4 * 8 + half * 4);
+                            const int4 r4 = *(const int4*)(gk + BN + kb * 32 + e4 * 8 + half * 4);
+                            const int gv[4] = {g4.x, g4.y, g4.z, g4.w};
+                            const int rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                            for (int e3 = 0; e3 < 4; e3++) {
+#pragma unroll
+                                for (int qb = 0; qb < QB; qb++) {
+                                    const bool inband =
+                                        (unsigned)(rv[e3] - qres[qb] + p.wl) <= span;
+                                    const bool ok = gv[e3] >= 0 && !inband &&
+                                                    (!p.causal || gv[e3] <= qpos[qb]);
+                                    if (!ok) s[qb][kb][e4 * 4 + e3] = -INFINITY;
+                                }
+                            }
+                        }
                 }
             }
-            // online softmax
+            // online softmax: running max first, then per 16-key step the bf16
+            // weights (B operand of P V) and their sum
+            float m_use[QB];
 #pragma unroll
             for (int qb = 0; qb < QB; qb++) {
                 float mx = s[qb][0][0];
@@ -239,41 +314,40 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 for (int e = 0; e < 16; e++) mx = fmaxf(mx, s[qb][1][e]);
                 mx = wave_max_xor32(mx) * c;
                 const bool up = mx > m_run[qb] + kLazyRescale;
-                const float m_use = up ? mx : m_run[qb];
+                m_use[qb] = up ? mx : m_run[qb];
                 if (__any(up)) {
-                    const float alpha = fast_exp2(m_run[qb] - m_use);
+                    const float alpha = fast_exp2(m_run[qb] - m_use[qb]);
                     l_run[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; db++) oacc[qb][db] *= alpha;
                 }
-                m_run[qb] = m_use;
-                float ls = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-                    for (int e = 0; e < 16; e++) {
-                        const float pe = fast_exp2(__builtin_fmaf(s[qb][kb][e], c, -m_use));
-                        s[qb][kb][e] = pe;
-                        ls += pe;
-                    }
-                l_run[qb] += ls;
+                m_run[qb] = m_use[qb];
             }
-            // O^T += V^T P^T : four 16-key steps
+            // O^T += V^T P^T : four 16-key steps; V^T through transposing reads
+            const int key_l = half * 4 + ((lane & 15) >> 2);
+            const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 bf16x8 pb[QB];
 #pragma unroll
-                for (int qb = 0; qb < QB; qb++)
+                for (int qb = 0; qb < QB; qb++) {
 #pragma unroll
                     for (int e = 0; e < 8; e++)
-                        pb[qb][e] = (__bf16)s[qb][t >> 1][(t & 1) * 8 + e];
-                const int key1 = t * 16 + half * 4 + ((lane & 15) >> 2);
-                const int colo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                        pb[qb][e] = (__bf16)fast_exp2(
+                            __builtin_fmaf(s[qb][t >> 1][(t & 1) * 8 + e], c, -m_use[qb]));
+                    float ls = l_run[qb];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const bf16x2 pr = {pb[qb][2 * e], pb[qb][2 * e + 1]};
+                        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+                    }
+                    l_run[qb] = ls;
+                }
 #pragma unroll
                 for (int db = 0; db < DB; db++) {
-                    const int col = db * 32 + colo;
-                    const i16x4 lo = lds_read_tr16(Vs + key1 * T::PITCH + col);
-                    const i16x4 hi = lds_read_tr16(Vs + (key1 + 8) * T::PITCH + col);
+                    const unsigned short* vp = Vs + (t * 16 + key_l) * T::VP + db * 32 + col_l;
+                    const i16x4 lo = lds_read_tr16(vp);
+                    const i16x4 hi = lds_read_tr16(vp + 8 * T::VP);
                     const bf16x8 a = __builtin_bit_cast(
                         bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -283,7 +357,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 }
             }
         }
-        if (has_next) store_tile_lds<D>(kr, vr, k_lds(st ^ 1), v_lds(st ^ 1));
+        if (has_next) store_tile<D>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
     }
 
@@ -341,8 +415,6 @@ hipError_t launch_d(const FwdParams& p, hipStream_t s) {
 }
 
 }  // namespace
-
-int fwd_bf16_rows_per_wave() { return 32; }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s) {
     if (D == 128) return launch_d<128, 1>(p, s);
