@@ -1,7 +1,10 @@
 // fwd_bf16.hip -- sliding-window attention forward, bf16 inputs, gfx950 MFMA.
 //
-// Each workgroup (4 waves) owns a tile of query positions of one residue class
-// r = i mod d for one kv head and `hpw` query heads of its group.  Inside a
+// Each workgroup owns a tile of query positions of one residue class r = i mod
+// d for one kv head and `hpw` query heads of its group: eight waves when four
+// query heads share the kv head (two 32-position row blocks per head, so every
+// K/V tile staged in LDS serves 256 query rows), four waves otherwise.  Each
+// wave holds 32 query rows of one head.  Inside a
 // residue class the dilated window i + t*d (mhpn.cn "Dilated sliding window",
 // section 2) is an ordinary window over m = (i - r) / d, so every gathered
 // Q/K/V row is a whole contiguous head vector and the tiles stay dense
@@ -15,7 +18,9 @@
 // v_mfma_f32_32x32x16_bf16 so that each lane holds 32 keys of one query: the
 // softmax row reductions are in-lane plus one exchange with lane ^ 32.  The
 // probabilities are rounded to bf16 and multiplied with V^T, read from the
-// natural-layout V tile through ds_read_b64_tr_b16.  The softmax is kept
+// natural-layout V tile through ds_read_b64_tr_b16.  K fragments are read
+// from LDS in batches ahead of their MFMAs, and a step's V fragments ahead of
+// its exponentials, so LDS latency overlaps other work.  The softmax is kept
 // online (running max m, sum l, rescaled accumulator), with the max moved only
 // when a tile exceeds it by more than 2^8, which is exact up to rounding; the
 // running sum adds the bf16-rounded weights, the same ones the products with
@@ -34,51 +39,44 @@
 #include "fwd_common.h"
 #include "swa_kernels.h"
 
-// LDS row pitches (bf16 elements).  K rows are read 16 B per lane, 16 rows per
-// LDS cycle: a pitch of 4 (mod 64) dwords puts those rows on distinct banks.
-// V rows are read by ds_read_b64_tr_b16, 4 rows x 64 B per 32 lanes: a pitch
-// of 16 (mod 64) dwords keeps those on distinct banks.
-#ifndef SWA_FWD_KPAD
-#define SWA_FWD_KPAD 8
-#endif
 
 namespace swa {
 namespace {
 
 constexpr int BN = 64;        // keys per K/V tile
-constexpr int NTHREADS = 256; // 4 waves
+constexpr int kQB = 1;  // 32-query blocks per wave
 constexpr int kFarAway = -(1 << 30);  // residue coordinate outside every window
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int D>
+template <int D, int NW>
 struct TileCfg {
-    static constexpr int KP = D + SWA_FWD_KPAD;                 // K row pitch
-#ifdef SWA_FWD_VPAD
-    static constexpr int VP = D + SWA_FWD_VPAD;
-#else
+    static constexpr int NT = 64 * NW;                          // threads per workgroup
+    // LDS row pitches (bf16 elements).  K rows are read 16 B per lane, 16
+    // rows per LDS cycle: a pitch of 4 (mod 64) dwords puts those rows on
+    // distinct banks.  V rows are read by ds_read_b64_tr_b16, 4 rows x 64 B per
+    // 32 lanes: a pitch of 16 (mod 64) dwords keeps those on distinct banks.
+    static constexpr int KP = D + 8;
     static constexpr int VP = ((D + 95) / 128) * 128 + 32;       // = 32 (mod 128)
-#endif
     static constexpr int K_ELEMS = BN * KP;
     static constexpr int V_ELEMS = BN * VP;
     static constexpr int STAGE = K_ELEMS + V_ELEMS;
     static constexpr int CPR = D / 8;                            // 16-byte chunks per row
-    static constexpr int PER_THREAD = BN * CPR / NTHREADS;
-    static constexpr int KEY_STEP = NTHREADS / CPR;              // rows between a thread's chunks
-    static_assert(PER_THREAD * NTHREADS == BN * CPR, "tile does not split evenly");
+    static constexpr int PER_THREAD = BN * CPR / NT;
+    static constexpr int KEY_STEP = NT / CPR;                    // rows between a thread's chunks
+    static_assert(PER_THREAD * NT == BN * CPR, "tile does not split evenly");
 };
 
 // Loads tile j of the key stream into registers (zero rows for padding).
 // For gathered global-key tiles it also records, per key, the position and
 // the residue coordinate g / d when g is in this residue class (else a value
 // no window reaches) in gk[2][BN], for the element masks.
-template <int D, bool GROWS>
-__device__ __forceinline__ void load_tile(u32x4 (&kr)[TileCfg<D>::PER_THREAD],
-                                          u32x4 (&vr)[TileCfg<D>::PER_THREAD],
+template <class T, bool GROWS>
+__device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
+                                          u32x4 (&vr)[T::PER_THREAD],
                                           const __bf16* kbase, const __bf16* vbase,
                                           int rowstride, const KeyStream& ks, const FwdParams& p,
                                           int j, int* gk) {
-    using T = TileCfg<D>;
     const int key0 = threadIdx.x / T::CPR;
     const int c = threadIdx.x % T::CPR;
     int kpos[T::PER_THREAD];
@@ -116,11 +114,10 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[TileCfg<D>::PER_THREAD],
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const u32x4 (&kr)[TileCfg<D>::PER_THREAD],
-                                           const u32x4 (&vr)[TileCfg<D>::PER_THREAD],
+template <class T>
+__device__ __forceinline__ void store_tile(const u32x4 (&kr)[T::PER_THREAD],
+                                           const u32x4 (&vr)[T::PER_THREAD],
                                            unsigned short* stage) {
-    using T = TileCfg<D>;
     const int key0 = threadIdx.x / T::CPR;
     const int c = threadIdx.x % T::CPR;
 #pragma unroll
@@ -133,10 +130,10 @@ __device__ __forceinline__ void store_tile(const u32x4 (&kr)[TileCfg<D>::PER_THR
 
 // GROWS = false: band workgroups (plus global key columns).
 // GROWS = true : global query rows over one key chunk, partial output.
-template <int D, int QB, bool GROWS>
-__global__ __launch_bounds__(NTHREADS, QB == 1 ? 2 : 1)
+template <int D, int QB, int NW, bool GROWS>
+__global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1)
 void swa_fwd_bf16_kernel(const FwdParams p) {
-    using T = TileCfg<D>;
+    using T = TileCfg<D, NW>;
     constexpr int KC = D / 16;   // 16-deep k-steps of QK^T
     constexpr int DB = D / 32;   // 32-row blocks of O^T
 
@@ -149,7 +146,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     const int half = lane >> 5;
 
     // ---- work item ---------------------------------------------------------
-    const WorkItem wi = GROWS ? decode_grows_item(p, blockIdx.x, (4 / p.hpw) * 32 * QB, BN)
+    const WorkItem wi = GROWS ? decode_grows_item(p, blockIdx.x, (NW / p.hpw) * 32 * QB, BN)
                               : decode_band_item(p, xcd_contiguous(blockIdx.x, gridDim.x), BN);
     const int b = wi.b, kvh = wi.kvh, hg = wi.hg, chunk = wi.chunk;
     const KeyStream& ks = wi.ks;
@@ -201,8 +198,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     // ---- prologue: tile 0 into stage 0 ---------------------------------------
     u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
     if (ks.n_tiles > 0) {
-        load_tile<D, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, 0, gk_lds[0]);
-        store_tile<D>(kr, vr, smem);
+        load_tile<T, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, 0, gk_lds[0]);
+        store_tile<T>(kr, vr, smem);
     }
     __syncthreads();
 
@@ -210,7 +207,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         const int st = j & 1;
         const bool has_next = j + 1 < ks.n_tiles;
         if (has_next)
-            load_tile<D, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, j + 1, gk_lds[st ^ 1]);
+            load_tile<T, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, j + 1, gk_lds[st ^ 1]);
 
         // classify this tile for this wave (wave-uniform)
         const bool band_tile = GROWS || j < ks.n_band_tiles;
@@ -231,17 +228,27 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 s[qb][0] = f32x16{};
                 s[qb][1] = f32x16{};
             }
+            // K fragments are read in batches of KBATCH ahead of their MFMAs so
+            // that LDS latency overlaps the matrix work
+            constexpr int KBATCH = 2 * KC < 16 ? 2 * KC : 16;
 #pragma unroll
-            for (int kc = 0; kc < KC; kc++) {
+            for (int k0 = 0; k0 < KC; k0 += KBATCH / 2) {
+                bf16x8 a[KBATCH];
 #pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    const bf16x8 a =
-                        *(const bf16x8*)(Ks + (kb * 32 + l32) * T::KP + kc * 16 + half * 8);
+                for (int i = 0; i < KBATCH; i++) {
+                    const int kc = k0 + i / 2, kb = i % 2;
+                    a[i] = *(const bf16x8*)(Ks + (kb * 32 + l32) * T::KP + kc * 16 + half * 8);
+                }
+#pragma unroll
+                for (int i = 0; i < KBATCH; i++) {
+                    const int kc = k0 + i / 2, kb = i % 2;
 #pragma unroll
                     for (int qb = 0; qb < QB; qb++)
-                        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][kc],
+                        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qreg[qb][kc],
                                                                             s[qb][kb], 0, 0, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, KBATCH, 0);       // DS reads first
+                __builtin_amdgcn_sched_group_barrier(0x008, KBATCH * QB, 0);  // then MFMAs
             }
             // Element masks.  Lane key offsets within the tile are
             // kb*32 + (e>>2)*8 + half*4 + (e&3); all compares are per element.
@@ -256,23 +263,27 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
                             for (int e = 0; e < 16; e++) {
                                 const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
-                                if (ko > lim) s[qb][kb][e] = -INFINITY;
+                                const int bad = (lim - ko) >> 31;
+                                s[qb][kb][e] += __builtin_bit_cast(float, bad & 0xff800000);
                             }
                     }
                 } else if (band_tile) {
 #pragma unroll
                     for (int qb = 0; qb < QB; qb++) {
-                        // dl = key - query; valid when -wl <= dl <= wr and key <= k_hi
+                        // x = key - query + wl must lie in [0, wl + wr] and the key
+                        // must not pass k_hi; a negative x | (span - x) | (lim - ko)
+                        // flags a violation.  Integer arithmetic only, so the masks
+                        // need no scalar condition registers.
                         const int base = kt0 + half * 4 - qres[qb] + p.wl;
-                        const unsigned span = (unsigned)(p.wl + p.wr);
+                        const int sb = p.wl + p.wr - base;
                         const int lim = ks.k_hi - kt0 - half * 4;
 #pragma unroll
                         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                             for (int e = 0; e < 16; e++) {
                                 const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
-                                const bool ok = (unsigned)(base + ko) <= span && ko <= lim;
-                                if (!ok) s[qb][kb][e] = -INFINITY;
+                                const int bad = ((base + ko) | (sb - ko) | (lim - ko)) >> 31;
+                                s[qb][kb][e] += __builtin_bit_cast(float, bad & 0xff800000);
                             }
                     }
                 } else {
@@ -328,6 +339,17 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
+                // V^T fragments of this step first: their LDS latency overlaps the
+                // exponentials below
+                bf16x8 va[DB];
+#pragma unroll
+                for (int db = 0; db < DB; db++) {
+                    const unsigned short* vp = Vs + (t * 16 + key_l) * T::VP + db * 32 + col_l;
+                    const i16x4 lo = lds_read_tr16(vp);
+                    const i16x4 hi = lds_read_tr16(vp + 8 * T::VP);
+                    va[db] = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
                 bf16x8 pb[QB];
 #pragma unroll
                 for (int qb = 0; qb < QB; qb++) {
@@ -344,20 +366,14 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                     l_run[qb] = ls;
                 }
 #pragma unroll
-                for (int db = 0; db < DB; db++) {
-                    const unsigned short* vp = Vs + (t * 16 + key_l) * T::VP + db * 32 + col_l;
-                    const i16x4 lo = lds_read_tr16(vp);
-                    const i16x4 hi = lds_read_tr16(vp + 8 * T::VP);
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                for (int db = 0; db < DB; db++)
 #pragma unroll
                     for (int qb = 0; qb < QB; qb++)
                         oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            a, pb[qb], oacc[qb][db], 0, 0, 0);
-                }
+                            va[db], pb[qb], oacc[qb][db], 0, 0, 0);
             }
         }
-        if (has_next) store_tile<D>(kr, vr, smem + (st ^ 1) * T::STAGE);
+        if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
     }
 
@@ -403,22 +419,35 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     }
 }
 
-template <int D, int QB>
+template <int D, int QB, int NW>
 hipError_t launch_d(const FwdParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, false>), dim3(p.n_blocks), dim3(NTHREADS), 0,
-                       s, p);
+    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, false>), dim3(p.n_blocks), dim3(64 * NW),
+                       0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_global == 0) return e;
     const int grid = p.B * p.Hkv * p.head_groups * p.g_rowgroups * p.g_nchunks;
-    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, true>), dim3(grid), dim3(NTHREADS), 0, s, p);
+    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, true>), dim3(grid), dim3(64 * NW), 0, s,
+                       p);
     return hipGetLastError();
 }
 
+// Waves per workgroup: eight when four query heads share the K/V tiles (the
+// tiles then serve two 32-position row blocks of each head), else four.
+int waves_per_wg(int hpw) { return hpw == 4 ? 8 : 4; }
+
 }  // namespace
 
+FwdShape fwd_bf16_shape(int group) {
+    // heads of one GQA group share the K/V tiles of a workgroup
+    const int hpw = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    const int rows = (waves_per_wg(hpw) / hpw) * 32 * kQB;
+    return FwdShape{hpw, rows, rows};
+}
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s) {
-    if (D == 128) return launch_d<128, 1>(p, s);
-    return launch_d<64, 1>(p, s);
+    const bool w8 = waves_per_wg(p.hpw) == 8;
+    if (D == 128) return w8 ? launch_d<128, kQB, 8>(p, s) : launch_d<128, kQB, 4>(p, s);
+    return w8 ? launch_d<64, kQB, 8>(p, s) : launch_d<64, kQB, 4>(p, s);
 }
 
 }  // namespace swa

@@ -40,8 +40,6 @@ void decode_splits(int B, int Hq, int W, int* splits, int* per_split) {
     *splits = (int)cdiv(W, ps);
 }
 
-int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
-
 }  // namespace
 
 extern "C" {
@@ -111,13 +109,10 @@ int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
     p.scale_log2 = scale * kLog2e;
     p.qd = N / dilation;
     p.rem = N % dilation;
-    if (dtype == SWA_BF16) {
-        p.hpw = gcd(p.group, 4);
-        p.bmq = (4 / p.hpw) * 32;
-    } else {
-        p.hpw = 1;
-        p.bmq = 64;
-    }
+    const swa::FwdShape shape =
+        dtype == SWA_BF16 ? swa::fwd_bf16_shape(p.group) : swa::fwd_f32_shape(p.group);
+    p.hpw = shape.hpw;
+    p.bmq = shape.bmq;
     p.head_groups = p.group / p.hpw;
     p.tiles_long = (int)cdiv(p.qd + 1, p.bmq);
     p.tiles_short = (int)cdiv(p.qd, p.bmq);
@@ -131,8 +126,7 @@ int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
     p.n_global = (int)g.size();
     for (int i = 0; i < p.n_global; i++) p.gpos[i] = g[i];
     global_chunks(N, &p.g_chunk, &p.g_nchunks);
-    const int rows_wg = dtype == SWA_BF16 ? (4 / p.hpw) * 32 : 64;
-    p.g_rowgroups = (int)cdiv(p.n_global, rows_wg);
+    p.g_rowgroups = (int)cdiv(p.n_global, shape.grows_rows);
 
     hipError_t e = dtype == SWA_BF16 ? swa::launch_fwd_bf16(p, D, stream)
                                      : swa::launch_fwd_f32(p, D, stream);

@@ -76,6 +76,17 @@ struct CombineParams {
     int32_t gpos[SWA_MAX_GLOBAL];
 };
 
+// Workgroup shape of a forward kernel for a GQA group size: query heads per
+// workgroup, query positions (of one residue class) per workgroup, and global
+// query rows per workgroup in the global-row pass.
+struct FwdShape {
+    int hpw;
+    int bmq;
+    int grows_rows;
+};
+FwdShape fwd_bf16_shape(int group);
+FwdShape fwd_f32_shape(int group);
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
