@@ -29,6 +29,31 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+FWD_SOURCES = ["sliding_window_attention_tiled_amd/csrc/fwd_bf16.hip",
+               "sliding_window_attention_tiled_amd/csrc/fwd_common.h",
+               "sliding_window_attention_tiled_amd/csrc/device_common.h",
+               "sliding_window_attention_tiled_amd/csrc/swa_kernels.h"]
+FWD_PROFILE = "profiles/swa_fwd_bf16_mistral_causal_w4096.md"
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed counter summary, or None
+    when the kernel sources changed after the counters were taken."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, FWD_PROFILE)).read()
+        h = hashlib.sha256()
+        for f in FWD_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic-bytes-per-launch: ", "source-sha256: ")))
+    if fields.get("source-sha256", "").strip() != h.hexdigest():
+        return None
+    return float(fields["traffic-bytes-per-launch"])
+
+
 def exact_pairs_causal(N: int, W: int) -> int:
     """Sum over i of |[max(0, i-W+1), i]|."""
     full = max(0, N - (W - 1))
@@ -226,7 +251,7 @@ def main():
         "kernel_ms": round(ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(exact_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(exact_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(exact_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic()},
     }
     if not args.no_decode and args.only is None:
         res["decode"] = bench_decode(args)
