@@ -77,6 +77,9 @@ enum {
 /* Largest number of distinct global positions one swa_fwd call accepts. */
 #define SWA_MAX_GLOBAL 256
 
+/* Longest sequence one swa_fwd call accepts (2^28 positions). */
+#define SWA_MAX_N (1 << 28)
+
 /*
  * swa_fwd: sliding-window attention over whole sequences (prefill / encoder).
  *
@@ -97,7 +100,8 @@ enum {
  *               query rows, which are split over the keys and merged).  Two
  *               calls in flight at once must not share it.
  *
- * Errors: SWA_ERR_ARG for null q/k/v/out, non-positive sizes, Hq % Hkv != 0,
+ * Errors: SWA_ERR_ARG for null q/k/v/out, non-positive sizes, N > SWA_MAX_N,
+ * Hq % Hkv != 0,
  * negative windows, dilation < 1, a global index outside [0, N), n_global < 0
  * or global_idx NULL with n_global > 0; SWA_ERR_UNSUPPORTED for D not in
  * {64,128}, an unknown dtype or more than SWA_MAX_GLOBAL distinct globals;

@@ -290,7 +290,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                     // gathered global keys: visible unless already in the band,
                     // and (causal) not after the query
                     const int* gk = gk_lds[st];
-                    const unsigned span = (unsigned)(p.wl + p.wr);
+                    const int span = p.wl + p.wr;
+                    const int causal_mask = p.causal ? -1 : 0;
 #pragma unroll
                     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
@@ -303,11 +304,15 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                             for (int e3 = 0; e3 < 4; e3++) {
 #pragma unroll
                                 for (int qb = 0; qb < QB; qb++) {
-                                    const bool inband =
-                                        (unsigned)(rv[e3] - qres[qb] + p.wl) <= span;
-                                    const bool ok = gv[e3] >= 0 && !inband &&
-                                                    (!p.causal || gv[e3] <= qpos[qb]);
-                                    if (!ok) s[qb][kb][e4 * 4 + e3] = -INFINITY;
+                                    // hidden when padding (g < 0), already in the band
+                                    // (0 <= x <= span), or causal and after the query;
+                                    // integer arithmetic only, as for the band masks
+                                    const int x = rv[e3] - qres[qb] + p.wl;
+                                    const int inband = ~(x | (span - x)) >> 31;
+                                    const int future = causal_mask & ((qpos[qb] - gv[e3]) >> 31);
+                                    const int bad = (gv[e3] >> 31) | inband | future;
+                                    s[qb][kb][e4 * 4 + e3] +=
+                                        __builtin_bit_cast(float, bad & 0xff800000);
                                 }
                             }
                         }

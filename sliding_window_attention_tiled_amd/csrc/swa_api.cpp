@@ -14,7 +14,9 @@ using swa::CombineParams;
 using swa::DecodeParams;
 using swa::FwdParams;
 
-constexpr int kMaxN = 1 << 30;
+// Longest sequence accepted: keeps every position, window offset and the
+// kernels' out-of-window sentinel (-2^30) within 32-bit integer range.
+constexpr int kMaxN = SWA_MAX_N;
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool supported_d(int D) { return D == 64 || D == 128; }

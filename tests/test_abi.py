@@ -73,6 +73,7 @@ def fwd(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), ARG), (dict(k=None), ARG), (dict(v=None), ARG), (dict(out=None), ARG),
     (dict(B=0), ARG), (dict(N=0), ARG), (dict(Hq=0), ARG), (dict(Hkv=0), ARG),
+    (dict(N=(1 << 28) + 1), ARG),                                # above SWA_MAX_N
     (dict(Hq=6, Hkv=4), ARG), (dict(wl=-1), ARG), (dict(wr=-2), ARG), (dict(dil=0), ARG),
     (dict(ng=-1), ARG), (dict(ng=3), ARG),                       # NULL global_idx
     (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(dtype=7), UNSUP),
