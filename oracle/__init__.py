@@ -80,6 +80,11 @@ class OracleLib:
         lib.oracle_kv_append.restype = I
         lib.oracle_decode.argtypes = [P, P, P, I, P, P, I64, I64, I64, I64, I64, D, P, P]
         lib.oracle_decode.restype = I
+        lib.oracle_kv_append_chunk.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, I]
+        lib.oracle_kv_append_chunk.restype = I
+        lib.oracle_fwd_cached.argtypes = [P, P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I64,
+                                          I64, D, P, P]
+        lib.oracle_fwd_cached.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         self.lib = lib
@@ -170,6 +175,37 @@ class Ring:
                                            self.B, self.Hkv, self.W, self.D, self.dtype)
         if rc != 0:
             raise ValueError("invalid arguments to oracle_kv_append")
+
+    def append_chunk(self, k, v):
+        """Appends a chunk k, v [B,n,Hkv,D] (n single appends in token order)."""
+        k, _ = _as_input(k)
+        v, _ = _as_input(v)
+        n = k.shape[1]
+        rc = self.orc.lib.oracle_kv_append_chunk(_ptr(self.k), _ptr(self.v), _ptr(k), _ptr(v),
+                                                 _ptr(self.head), _ptr(self.len), self.B,
+                                                 self.Hkv, self.W, n, self.D, self.dtype)
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_kv_append_chunk")
+
+    def fwd_cached(self, q, k, v, *, win_left: int, scale=None):
+        """Causal window attention of a prompt chunk q [B,n,Hq,D], k/v [B,n,Hkv,D]
+        that follows the tokens held in this ring.  The ring is not modified.
+        Returns (out [B,n,Hq,D], lse [B,Hq,n]) fp64."""
+        q, _ = _as_input(q)
+        k, _ = _as_input(k)
+        v, _ = _as_input(v)
+        B, n, Hq, D = q.shape
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        out = np.zeros((B, n, Hq, D), np.float64)
+        lse = np.zeros((B, Hq, n), np.float64)
+        rc = self.orc.lib.oracle_fwd_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(self.k),
+                                            _ptr(self.v), self.dtype, _ptr(self.head),
+                                            _ptr(self.len), B, Hq, self.Hkv, n, self.W, D,
+                                            win_left, float(scale), _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_fwd_cached")
+        return out, lse
 
     def decode(self, q, scale=None):
         """q [B,Hq,D] -> (out [B,Hq,D], lse [B,Hq]) fp64."""

@@ -296,6 +296,115 @@ int oracle_decode(const void* q, const void* kcache, const void* vcache, int dty
     return 0;
 }
 
+/* ---- chunked prefill over the ring ----------------------------------- */
+
+/* Appends a chunk of n tokens, k, v [B,n,Hkv,D], to the ring: the same state
+ * as n single appends in token order (intelliparadigm.com, section 3.1, the
+ * RingBuffer class).  Token t lands in slot (ring_head + t) mod W; when n > W
+ * only the last W tokens survive, the older ones being overwritten within the
+ * chunk (aiqz.cc, "inference optimisation": the cache rolls, keeping only the
+ * last W entries).  Then ring_head advances by n (mod W) and cache_len grows
+ * by n, capped at W.  n == 0 changes nothing. */
+int oracle_kv_append_chunk(void* kcache, void* vcache, const void* k, const void* v,
+                           int64_t* ring_head, int64_t* cache_len,
+                           int64_t B, int64_t Hkv, int64_t W, int64_t n, int64_t D, int dtype) {
+    if (B <= 0 || Hkv <= 0 || W <= 0 || D <= 0 || n < 0 || (dtype != 0 && dtype != 1))
+        return -1;
+    for (int64_t b = 0; b < B; b++)
+        if (ring_head[b] < 0 || ring_head[b] >= W || cache_len[b] < 0 || cache_len[b] > W)
+            return -1;
+    const int64_t first = n > W ? n - W : 0; /* older tokens would be overwritten */
+    for (int64_t b = 0; b < B; b++) {
+        for (int64_t t = first; t < n; t++) {
+            int64_t slot = (ring_head[b] + t) % W;
+            for (int64_t h = 0; h < Hkv; h++)
+                for (int64_t c = 0; c < D; c++) {
+                    int64_t di = ((b * Hkv + h) * W + slot) * D + c;
+                    int64_t si = ((b * n + t) * Hkv + h) * D + c;
+                    copy_elem(kcache, k, dtype, di, si);
+                    copy_elem(vcache, v, dtype, di, si);
+                }
+        }
+        ring_head[b] = (ring_head[b] + n) % W;
+        cache_len[b] = cache_len[b] + n < W ? cache_len[b] + n : W;
+    }
+    return 0;
+}
+
+/* Causal sliding-window attention of a prompt chunk that follows the tokens
+ * held in the ring (streaming inference: aiqz.cc, "inference optimisation",
+ * third strategy; bmjup.com, Q&A "training vs inference": at inference only
+ * the window's keys and values are kept).
+ *
+ * The chunk holds n tokens: q [B,n,Hq,D], k, v [B,n,Hkv,D].  Let P be the
+ * position of chunk token 0; the ring of sequence b holds the cache_len[b]
+ * tokens before it, the one of age a (a = 0 newest) at position P - 1 - a in
+ * slot (ring_head[b] - 1 - a) mod W.  Query t of the chunk (position P + t)
+ * attends to every available key at positions P + t - wl .. P + t:
+ *   ring tokens of age a < cache_len[b] with a <= wl - 1 - t, and
+ *   chunk tokens j with max(0, t - wl) <= j <= t.
+ * out [B,n,Hq,D] and lse [B,Hq,n] in double.  Requires wl <= W, so that no
+ * key the window asks for could have been evicted while a ring slot was
+ * still free. */
+int oracle_fwd_cached(const void* q, const void* k, const void* v, const void* kcache,
+                      const void* vcache, int dtype, const int64_t* ring_head,
+                      const int64_t* cache_len, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                      int64_t W, int64_t D, int64_t wl, double scale, double* out,
+                      double* lse) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || n <= 0 || W <= 0 || D <= 0 ||
+        wl < 0 || wl > W || (dtype != 0 && dtype != 1))
+        return -1;
+    for (int64_t b = 0; b < B; b++)
+        if (ring_head[b] < 0 || ring_head[b] >= W || cache_len[b] < 0 || cache_len[b] > W)
+            return -1;
+    const int64_t group = Hq / Hkv;
+    const int64_t cap = W + wl + 1; /* room for every ring slot and window key */
+    const size_t esz = dtype == 0 ? 4 : 2;
+#pragma omp parallel
+    {
+        /* the query's keys and values gathered in attention order (exact
+         * copies of the stored elements), then one softmax row over them */
+        void* kt = malloc(esz * (size_t)(cap * D));
+        void* vt = malloc(esz * (size_t)(cap * D));
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+        double* s = (double*)malloc(sizeof(double) * (size_t)cap);
+        for (int64_t t = 0; t < cap; t++) keys[t] = t;
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t row = 0; row < B * n * Hq; row++) {
+            int64_t nk = 0;
+            int64_t h = row % Hq, t = (row / Hq) % n, b = row / (Hq * n), kh = h / group;
+            /* ring part, oldest first: ages a = a_max .. 0 */
+            int64_t a_max = wl - 1 - t;
+            if (a_max > cache_len[b] - 1) a_max = cache_len[b] - 1;
+            for (int64_t a = a_max; a >= 0; a--) {
+                int64_t slot = ((ring_head[b] - 1 - a) % W + W) % W;
+                int64_t base = ((b * Hkv + kh) * W + slot) * D;
+                for (int64_t c = 0; c < D; c++) {
+                    copy_elem(kt, kcache, dtype, nk * D + c, base + c);
+                    copy_elem(vt, vcache, dtype, nk * D + c, base + c);
+                }
+                nk++;
+            }
+            /* chunk part */
+            for (int64_t j = t - wl > 0 ? t - wl : 0; j <= t; j++) {
+                int64_t base = ((b * n + j) * Hkv + kh) * D;
+                for (int64_t c = 0; c < D; c++) {
+                    copy_elem(kt, k, dtype, nk * D + c, base + c);
+                    copy_elem(vt, v, dtype, nk * D + c, base + c);
+                }
+                nk++;
+            }
+            attend_row(q, ((b * n + t) * Hq + h) * D, kt, vt, 0, D, dtype, D, keys, nk, scale,
+                       s, out + ((b * n + t) * Hq + h) * D, lse + (b * Hq + h) * n + t);
+        }
+        free(kt);
+        free(vt);
+        free(keys);
+        free(s);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

@@ -326,8 +326,90 @@ def pin_decode(orc):
     _close(lse_a, lse_b, 1e-12, "ring rotation lse")
 
 
+# ---- chunked prefill handed to the ring --------------------------------------
+
+def _empty_ring(orc, B, Hkv, W, D, dtype, head):
+    z = np.zeros((B, Hkv, W, D), np.uint16 if dtype == "bf16" else np.float32)
+    return orc.ring(z, z.copy(), head, [0] * B)
+
+
+def pin_append_chunk(orc):
+    """A chunk append leaves the ring exactly as that many single appends."""
+    B, Hkv, W, D = 2, 2, 8, 4
+    rng = np.random.Generator(np.random.PCG64(21))
+    for n in (0, 1, 5, 8, 11, 19, 27):
+        kc = to_bf16_bits(rng.standard_normal((B, Hkv, W, D), dtype=np.float32))
+        vc = to_bf16_bits(rng.standard_normal((B, Hkv, W, D), dtype=np.float32))
+        head, length = [3, 6], [2, W]
+        a = orc.ring(kc, vc, head, length)
+        b = orc.ring(kc, vc, head, length)
+        k = to_bf16_bits(rng.standard_normal((B, n, Hkv, D), dtype=np.float32))
+        v = to_bf16_bits(rng.standard_normal((B, n, Hkv, D), dtype=np.float32))
+        a.append_chunk(k, v)
+        for t in range(n):
+            b.append(np.ascontiguousarray(k[:, t]), np.ascontiguousarray(v[:, t]))
+        assert np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v), f"n={n} contents"
+        assert a.head.tolist() == b.head.tolist(), f"n={n} head"
+        assert a.len.tolist() == b.len.tolist(), f"n={n} len"
+
+
+CHUNK_CASES = [
+    # (B, Hq, Hkv, D, W, wl, chunk lengths, dtype)
+    (1, 2, 2, 8, 16, 15, [40], "f32"),                  # one chunk, empty ring
+    (1, 2, 1, 8, 16, 15, [7, 1, 30, 9], "bf16"),        # GQA 2, chunks < and > W
+    (2, 4, 2, 8, 12, 5, [3, 20, 1, 1, 14], "bf16"),     # ring wider than the window
+    (1, 2, 2, 8, 9, 9, [9, 9, 9], "f32"),               # wl == W, chunk == W
+]
+
+
+def pin_chunked_prefill(orc):
+    """Running a prompt chunk by chunk through the ring (attend, then append)
+    gives the causal window attention of the whole prompt (dense-mask brute
+    force over the full sequence)."""
+    for n_case, (B, Hq, Hkv, D, W, wl, chunks, dt) in enumerate(CHUNK_CASES):
+        N = sum(chunks)
+        q, k, v = fwd_inputs(300 + n_case, B, Hq, Hkv, N, D, dt)
+        ref_o, ref_l = bruteforce.fwd(q, k, v, win_left=wl, win_right=0, scale=0.3)
+        ring = _empty_ring(orc, B, Hkv, W, D, dt, [n_case % W] * B)
+        p0 = 0
+        for n in chunks:
+            sl = slice(p0, p0 + n)
+            cq, ck, cv = (np.ascontiguousarray(x[:, sl]) for x in (q, k, v))
+            o, l = ring.fwd_cached(cq, ck, cv, win_left=wl, scale=0.3)
+            _close(o, ref_o[:, sl], 1e-12, f"chunked prefill case {n_case} out @{p0}")
+            _close(l, ref_l[:, :, sl], 1e-12, f"chunked prefill case {n_case} lse @{p0}")
+            ring.append_chunk(ck, cv)
+            p0 += n
+        assert ring.len.tolist() == [min(N, W)] * B
+
+
+def pin_prefill_then_decode(orc):
+    """Chunked prefill of a prompt, then decode steps on the same ring: every
+    step equals the causal window-W attention row of the whole sequence."""
+    B, Hq, Hkv, D, W = 1, 4, 2, 8, 10
+    chunks, steps = [6, 13], 5
+    N = sum(chunks) + steps
+    q, k, v = fwd_inputs(310, B, Hq, Hkv, N, D, "bf16")
+    ref_o, ref_l = bruteforce.fwd(q, k, v, win_left=W - 1, win_right=0, scale=0.4)
+    ring = _empty_ring(orc, B, Hkv, W, D, "bf16", [4])
+    p0 = 0
+    for n in chunks:
+        sl = slice(p0, p0 + n)
+        cq, ck, cv = (np.ascontiguousarray(x[:, sl]) for x in (q, k, v))
+        o, _ = ring.fwd_cached(cq, ck, cv, win_left=W - 1, scale=0.4)
+        _close(o, ref_o[:, sl], 1e-12, "prefill chunk")
+        ring.append_chunk(ck, cv)
+        p0 += n
+    for t in range(p0, N):
+        ring.append(np.ascontiguousarray(k[:, t]), np.ascontiguousarray(v[:, t]))
+        o, l = ring.decode(np.ascontiguousarray(q[:, t]), scale=0.4)
+        _close(o, ref_o[:, t], 1e-12, f"decode step at {t}")
+        _close(l, ref_l[:, :, t], 1e-12, f"decode lse at {t}")
+
+
 ALL_PINS = [
     pin_dilated_index_sets, pin_dilated_span, pin_edge_truncation, pin_decode_demo_window,
     pin_ring_buffer_trace, pin_bruteforce, pin_bruteforce_mask_is_page_mask, pin_full_window,
     pin_zero_window, pin_q_zero, pin_dilation_strided, pin_gqa, pin_globals, pin_decode,
+    pin_append_chunk, pin_chunked_prefill, pin_prefill_then_decode,
 ]

@@ -45,6 +45,22 @@ MUTATIONS = {
                            "cache_len[b] = cache_len[b] + 1;"),
     "decode_kv_head_modulo": ("int64_t b = bh / Hq, h = bh % Hq, kh = h / group;",
                               "int64_t b = bh / Hq, h = bh % Hq, kh = h % Hkv;"),
+    "cached_age_limit_off_by_one": ("int64_t a_max = wl - 1 - t;", "int64_t a_max = wl - t;"),
+    "cached_ring_slot_newest_missed": (
+        "int64_t slot = ((ring_head[b] - 1 - a) % W + W) % W;\n                int64_t base",
+        "int64_t slot = ((ring_head[b] - a) % W + W) % W;\n                int64_t base"),
+    "cached_chunk_window_short": ("for (int64_t j = t - wl > 0 ? t - wl : 0; j <= t; j++)",
+                                  "for (int64_t j = t - wl + 1 > 0 ? t - wl + 1 : 0; j <= t; j++)"),
+    "cached_ring_ignores_len": ("if (a_max > cache_len[b] - 1) a_max = cache_len[b] - 1;",
+                                "if (a_max > W - 1) a_max = W - 1;"),
+    "cached_kv_head_modulo": ("b = row / (Hq * n), kh = h / group;",
+                              "b = row / (Hq * n), kh = h % Hkv;"),
+    "chunk_survivors_from_head": ("int64_t slot = (ring_head[b] + t) % W;",
+                                  "int64_t slot = (ring_head[b] + t - first) % W;"),
+    "chunk_head_advance_capped": ("ring_head[b] = (ring_head[b] + n) % W;",
+                                  "ring_head[b] = (ring_head[b] + (n < W ? n : W)) % W;"),
+    "chunk_len_uncapped": ("cache_len[b] = cache_len[b] + n < W ? cache_len[b] + n : W;",
+                           "cache_len[b] = cache_len[b] + n;"),
 }
 
 
