@@ -128,8 +128,9 @@ size_t swa_fwd_workspace_size(int B, int Hq, int N, int D, int n_global);
  *   kcache, vcache   device, [B, Hkv, W, D] of `dtype` (updated in place)
  *   k_new, v_new     device, [B, Hkv, D] of `dtype`
  *   ring_head, cache_len   device int32 [B] (updated in place); on entry
- *                    0 <= ring_head < W and 0 <= cache_len <= W (not checked
- *                    on the device: out-of-range values are the caller's error)
+ *                    0 <= ring_head < W and 0 <= cache_len <= W.  Values out
+ *                    of range are the caller's error; the kernels clamp them
+ *                    into range so that no access leaves the ring.
  *
  * Errors: SWA_ERR_ARG for null pointers or non-positive sizes;
  * SWA_ERR_UNSUPPORTED for D or dtype; SWA_ERR_HIP if the launch fails.
@@ -137,6 +138,63 @@ size_t swa_fwd_workspace_size(int B, int Hq, int N, int D, int n_global);
 int swa_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_new,
                   int32_t* ring_head, int32_t* cache_len,
                   int B, int Hkv, int W, int D, int dtype, hipStream_t stream);
+
+/*
+ * swa_kv_append_chunk: append n tokens per sequence to the ring at once, with
+ * the same result as n calls of swa_kv_append in token order
+ * (intelliparadigm.com, section 3.1, RingBuffer; aiqz.cc, "inference
+ * optimisation": the cache rolls and keeps the last W entries).  Token t of
+ * the chunk goes to slot (ring_head[b] + t) % W; when n > W only the last W
+ * tokens are written.  Then ring_head[b] = (ring_head[b] + n) % W and
+ * cache_len[b] = min(cache_len[b] + n, W).  Used to hand a prefilled prompt
+ * (or one chunk of it) over to decode.
+ *
+ *   kcache, vcache   device, [B, Hkv, W, D] of `dtype` (updated in place)
+ *   k, v             device, [B, n, Hkv, D] of `dtype` (the layout of swa_fwd's k, v);
+ *                    may be NULL when n == 0
+ *   ring_head, cache_len   device int32 [B], as for swa_kv_append
+ *   n                tokens per sequence, 0 <= n <= SWA_MAX_N (0: nothing to do)
+ *
+ * Errors: as swa_kv_append (k, v may be NULL only when n == 0), plus
+ * SWA_ERR_ARG for n < 0 or n or W above SWA_MAX_N.
+ */
+int swa_kv_append_chunk(void* kcache, void* vcache, const void* k, const void* v,
+                        int32_t* ring_head, int32_t* cache_len,
+                        int B, int Hkv, int W, int n, int D, int dtype, hipStream_t stream);
+
+/*
+ * swa_fwd_cached: causal sliding-window attention of a prompt chunk that
+ * follows the tokens held in the ring (streaming prefill: aiqz.cc, "inference
+ * optimisation", third strategy; bmjup.com, Q&A "training vs inference").
+ * Let P be the position of chunk token 0; the ring of sequence b holds the
+ * cache_len[b] tokens before it, the one of age a (0 = newest, position
+ * P - 1 - a) in slot (ring_head[b] - 1 - a) mod W.  Query t of the chunk
+ * attends to every held key at positions P + t - win_left .. P + t:
+ *   ring entries of age a < cache_len[b] with a <= win_left - 1 - t, and
+ *   chunk tokens j with max(0, t - win_left) <= j <= t.
+ * The ring is read only; append the chunk afterwards (swa_kv_append_chunk)
+ * to continue with the next chunk or with decode.  No dilation and no global
+ * tokens on this path.
+ *
+ *   q, out      device, [B, n, Hq, D] of `dtype`
+ *   k, v        device, [B, n, Hkv, D] of `dtype` (the chunk's own keys/values)
+ *   kcache, vcache, ring_head, cache_len   device, as for swa_kv_append
+ *   lse         device, [B, Hq, n] float32 (may be NULL)
+ *   n           chunk length, 1 <= n <= SWA_MAX_N
+ *   win_left    keys before the query, 0 <= win_left <= W (older keys could
+ *               have left the ring)
+ *   scale       multiplier of q.k (1/sqrt(D) for the usual scaling)
+ *
+ * Errors: SWA_ERR_ARG for null pointers (lse excepted), non-positive sizes,
+ * n or W above SWA_MAX_N, Hq % Hkv != 0, win_left < 0 or win_left > W;
+ * SWA_ERR_UNSUPPORTED for D or dtype; SWA_ERR_HIP if a launch fails.
+ */
+int swa_fwd_cached(const void* q, const void* k, const void* v,
+                   const void* kcache, const void* vcache,
+                   const int32_t* ring_head, const int32_t* cache_len,
+                   void* out, float* lse,
+                   int B, int Hq, int Hkv, int n, int W, int D,
+                   int win_left, float scale, int dtype, hipStream_t stream);
 
 /*
  * swa_decode: one query token per sequence attends over the valid ring slots

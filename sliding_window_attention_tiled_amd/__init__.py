@@ -6,6 +6,6 @@ The compute lives in the HIP library ``libswa.so`` behind the C ABI declared in
 call does, and fails loudly if it has not been built.
 """
 from .binding import (  # noqa: F401
-    SwaError, fwd, fwd_workspace_size, kv_append, decode, decode_workspace_size,
-    load_library,
+    SwaError, fwd, fwd_workspace_size, fwd_cached, kv_append, kv_append_chunk, decode,
+    decode_workspace_size, load_library,
 )

@@ -45,6 +45,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swa_fwd_workspace_size.restype = SZ
     lib.swa_kv_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
     lib.swa_kv_append.restype = I
+    lib.swa_kv_append_chunk.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.swa_kv_append_chunk.restype = I
+    lib.swa_fwd_cached.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.swa_fwd_cached.restype = I
     lib.swa_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P, SZ, I, P]
     lib.swa_decode.restype = I
     lib.swa_decode_workspace_size.argtypes = [I, I, I, I]
@@ -141,14 +145,70 @@ def kv_append(kcache: torch.Tensor, vcache: torch.Tensor, k_new: torch.Tensor,
     B, Hkv, W, D = kcache.shape
     if vcache.shape != kcache.shape or k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
         raise SwaError(-1, "kv_append shape mismatch")
-    for t, name in ((ring_head, "ring_head"), (cache_len, "cache_len")):
-        if t.dtype != torch.int32 or t.shape != (B,):
-            raise SwaError(-1, f"{name} must be int32 [B]")
+    _ring_state(ring_head, cache_len, B)
     st = lib.swa_kv_append(_dev(kcache, "kcache"), _dev(vcache, "vcache"),
                            _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                            _dev(ring_head, "ring_head"), _dev(cache_len, "cache_len"),
                            B, Hkv, W, D, _dtype_code(kcache), _stream(kcache))
     _check(st, "swa_kv_append")
+
+
+def _ring_state(ring_head: torch.Tensor, cache_len: torch.Tensor, B: int):
+    for t, name in ((ring_head, "ring_head"), (cache_len, "cache_len")):
+        if t.dtype != torch.int32 or t.shape != (B,):
+            raise SwaError(-1, f"{name} must be int32 [B]")
+
+
+def kv_append_chunk(kcache: torch.Tensor, vcache: torch.Tensor, k: torch.Tensor,
+                    v: torch.Tensor, ring_head: torch.Tensor, cache_len: torch.Tensor):
+    """In-place append of a chunk k/v [B,n,Hkv,D] to the ring kcache/vcache
+    [B,Hkv,W,D] (the same result as n single appends)."""
+    lib = load_library()
+    B, Hkv, W, D = kcache.shape
+    n = k.shape[1]
+    if vcache.shape != kcache.shape or k.shape != (B, n, Hkv, D) or v.shape != k.shape:
+        raise SwaError(-1, "kv_append_chunk shape mismatch")
+    if k.dtype != kcache.dtype or v.dtype != kcache.dtype:
+        raise SwaError(-1, "chunk and ring must share one dtype")
+    _ring_state(ring_head, cache_len, B)
+    st = lib.swa_kv_append_chunk(_dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(k, "k"),
+                                 _dev(v, "v"), _dev(ring_head, "ring_head"),
+                                 _dev(cache_len, "cache_len"), B, Hkv, W, n, D,
+                                 _dtype_code(kcache), _stream(kcache))
+    _check(st, "swa_kv_append_chunk")
+
+
+def fwd_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kcache: torch.Tensor,
+               vcache: torch.Tensor, ring_head: torch.Tensor, cache_len: torch.Tensor, *,
+               win_left: int, scale: float | None = None, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, return_lse: bool = True):
+    """Causal window attention of a prompt chunk q [B,n,Hq,D], k/v [B,n,Hkv,D]
+    that follows the tokens held in the ring kcache/vcache [B,Hkv,W,D].
+    Returns (out [B,n,Hq,D], lse [B,Hq,n] fp32) or out alone."""
+    lib = load_library()
+    B, n, Hq, D = q.shape
+    Hkv, W = kcache.shape[1], kcache.shape[2]
+    if k.shape != (B, n, Hkv, D) or v.shape != k.shape:
+        raise SwaError(-1, "fwd_cached chunk shape mismatch")
+    if kcache.shape != (B, Hkv, W, D) or vcache.shape != kcache.shape:
+        raise SwaError(-1, "fwd_cached ring shape mismatch")
+    for t in (k, v, kcache, vcache):
+        if t.dtype != q.dtype:
+            raise SwaError(-1, "q, k, v and the ring must share one dtype")
+    _ring_state(ring_head, cache_len, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    st = lib.swa_fwd_cached(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(kcache, "kcache"),
+                            _dev(vcache, "vcache"), _dev(ring_head, "ring_head"),
+                            _dev(cache_len, "cache_len"), _dev(out, "out"), _dev(lse, "lse"),
+                            B, Hq, Hkv, n, W, D, win_left, float(scale), _dtype_code(q),
+                            _stream(q))
+    _check(st, "swa_fwd_cached")
+    return (out, lse) if return_lse else out
 
 
 def decode_workspace_size(B: int, Hq: int, W: int, D: int) -> int:

@@ -1,4 +1,4 @@
-"""The five workloads the library is measured and checked on.
+"""The workloads the library is measured and checked on.
 
 Window conventions (explicit left/right extents in dilated steps):
   * causal window of W keys  -> win_left = W - 1, win_right = 0
@@ -24,3 +24,8 @@ DILATED_STACK = dict(B=2, Hq=16, Hkv=16, N=32768, D=128, dtype="bf16",
                      seed=4)
 
 DECODE = dict(B=64, Hq=32, Hkv=8, W=4096, D=128, dtype="bf16", steps=256, seed=5)
+
+# chunked prefill: one 4096-token chunk of a Mistral-shaped prompt attending to
+# a full 4096-slot ring (the tokens before it) and to itself, window 4096
+PREFILL_CHUNK = dict(B=1, Hq=32, Hkv=8, W=4096, D=128, dtype="bf16", chunk=4096,
+                     win_left=4095, seed=6)

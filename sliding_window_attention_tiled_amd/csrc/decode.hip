@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(unsigned char* kc, unsig
                                                         int32_t* head, int32_t* len, int Hkv,
                                                         int W, int row_bytes) {
     const int b = blockIdx.x;
-    const int slot = head[b];
+    const int slot = min(max(head[b], 0), W - 1);  // device data: keep the write in the ring
     const int chunks = Hkv * row_bytes / 16;  // 16-byte chunks per tensor
     for (int ci = threadIdx.x; ci < chunks; ci += blockDim.x) {
         const int h = ci / (row_bytes / 16), c = ci % (row_bytes / 16);
@@ -41,8 +41,41 @@ __global__ __launch_bounds__(256) void kv_append_kernel(unsigned char* kc, unsig
     __syncthreads();
     if (threadIdx.x == 0) {
         head[b] = slot + 1 == W ? 0 : slot + 1;
-        len[b] = min(len[b] + 1, W);
+        len[b] = min(max(len[b], 0) + 1, W);
     }
+}
+
+// Chunk append: the last m = min(n, W) tokens of k, v [B][n][Hkv][row] go to
+// slots (ring_head + t) mod W (t = n - m .. n - 1), which is what n single
+// appends leave behind.  One thread per 16-byte piece, `bps` workgroups per
+// sequence; the state update runs as a second kernel so that every copy has
+// read the old ring_head.
+__global__ __launch_bounds__(256) void kv_append_chunk_kernel(
+    unsigned char* kc, unsigned char* vc, const unsigned char* k, const unsigned char* v,
+    const int32_t* head, int Hkv, int W, int n, int m, int row_bytes, int bps) {
+    const int b = blockIdx.x / bps;
+    const int cpr = row_bytes / 16;               // 16-byte chunks per row
+    const int64_t total = (int64_t)m * Hkv * cpr;  // chunks of this sequence
+    const int64_t ci = (int64_t)(blockIdx.x % bps) * blockDim.x + threadIdx.x;
+    if (ci >= total) return;
+    const int c = (int)(ci % cpr);
+    const int h = (int)((ci / cpr) % Hkv);
+    const int64_t t = n - m + ci / ((int64_t)cpr * Hkv);
+    const int64_t h0 = min(max(head[b], 0), W - 1);
+    const int64_t slot = (h0 + t) % W;
+    const size_t src = (((size_t)b * n + t) * Hkv + h) * row_bytes + c * 16;
+    const size_t dst = (((size_t)b * Hkv + h) * W + slot) * row_bytes + c * 16;
+    *(u32x4*)(kc + dst) = *(const u32x4*)(k + src);
+    *(u32x4*)(vc + dst) = *(const u32x4*)(v + src);
+}
+
+__global__ __launch_bounds__(64) void ring_advance_kernel(int32_t* head, int32_t* len, int B,
+                                                         int W, int n) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int64_t h0 = min(max(head[b], 0), W - 1);
+    head[b] = (int32_t)((h0 + n) % W);
+    len[b] = (int32_t)min<int64_t>((int64_t)max(len[b], 0) + n, W);
 }
 
 // ---- bf16 split decode on MFMA ----------------------------------------------------
@@ -387,6 +420,25 @@ hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn, 
     hipLaunchKernelGGL(kv_append_kernel, dim3(B), dim3(256), 0, s, (unsigned char*)kc,
                        (unsigned char*)vc, (const unsigned char*)kn, (const unsigned char*)vn,
                        head, len, Hkv, W, D * elem_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append_chunk(void* kc, void* vc, const void* k, const void* v,
+                                  int32_t* head, int32_t* len, int B, int Hkv, int W, int n,
+                                  int D, int elem_bytes, hipStream_t s) {
+    const int m = n < W ? n : W;
+    const int row_bytes = D * elem_bytes;
+    const int64_t chunks = (int64_t)m * Hkv * (row_bytes / 16);
+    const int64_t bps = (chunks + 255) / 256;  // workgroups per sequence
+    if (bps * B > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_append_chunk_kernel, dim3((unsigned)(bps * B)), dim3(256), 0, s,
+                       (unsigned char*)kc, (unsigned char*)vc, (const unsigned char*)k,
+                       (const unsigned char*)v, (const int32_t*)head, Hkv, W, n, m, row_bytes,
+                       (int)bps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ring_advance_kernel, dim3((B + 63) / 64), dim3(64), 0, s, head, len, B, W,
+                       n);
     return hipGetLastError();
 }
 

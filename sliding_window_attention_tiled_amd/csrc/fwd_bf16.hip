@@ -70,15 +70,40 @@ struct TileCfg {
 // Loads tile j of the key stream into registers (zero rows for padding).
 // For gathered global-key tiles it also records, per key, the position and
 // the residue coordinate g / d when g is in this residue class (else a value
-// no window reaches) in gk[2][BN], for the element masks.
+// no window reaches) in gk[2][BN], for the element masks.  Band tiles that
+// start at a negative coordinate (chunked prefill) take those keys from the
+// ring rows krbase / vrbase (row pitch D).
 template <class T, bool GROWS>
 __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
                                           u32x4 (&vr)[T::PER_THREAD],
                                           const __bf16* kbase, const __bf16* vbase,
+                                          const __bf16* krbase, const __bf16* vrbase,
                                           int rowstride, const KeyStream& ks, const FwdParams& p,
                                           int j, int* gk) {
     const int key0 = threadIdx.x / T::CPR;
     const int c = threadIdx.x % T::CPR;
+    if (!GROWS && j < ks.n_band_tiles && ks.k_lo + j * BN < 0) {
+        // d = 1 and r = 0 here: coordinate = position within the chunk
+        const int kk0 = ks.k_lo + j * BN + key0;
+#pragma unroll
+        for (int u = 0; u < T::PER_THREAD; u++) {
+            const int kk = kk0 + u * T::KEY_STEP;
+            const __bf16* ks_src = nullptr;
+            const __bf16* vs_src = nullptr;
+            if (kk < 0) {
+                const size_t off = (size_t)ring_slot(ks, kk, p.W) * T::CPR * 8 + c * 8;
+                ks_src = krbase + off;
+                vs_src = vrbase + off;
+            } else if (kk <= ks.k_hi) {
+                const size_t off = (size_t)kk * rowstride + c * 8;
+                ks_src = kbase + off;
+                vs_src = vbase + off;
+            }
+            kr[u] = ks_src ? *(const u32x4*)ks_src : u32x4{0u, 0u, 0u, 0u};
+            vr[u] = vs_src ? *(const u32x4*)vs_src : u32x4{0u, 0u, 0u, 0u};
+        }
+        return;
+    }
     int kpos[T::PER_THREAD];
     if (GROWS || j < ks.n_band_tiles) {
         const int kk0 = ks.k_lo + j * BN + key0;
@@ -157,6 +182,10 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     const int rowstride = p.Hkv * D;
     const __bf16* kbase = (const __bf16*)p.k + ((size_t)b * p.N * p.Hkv + kvh) * D;
     const __bf16* vbase = (const __bf16*)p.v + ((size_t)b * p.N * p.Hkv + kvh) * D;
+    // ring rows of this (b, kv head) for chunked prefill (unused otherwise)
+    const size_t ring_off = ((size_t)b * p.Hkv + kvh) * (size_t)p.W * D;
+    const __bf16* krbase = (const __bf16*)p.kring + ring_off;
+    const __bf16* vrbase = (const __bf16*)p.vring + ring_off;
 
     // ---- query rows of this wave (B operand of S^T = K Q^T) -------------------
     int qpos[QB];     // absolute position of the lane's query row, -1 if none
@@ -198,7 +227,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     // ---- prologue: tile 0 into stage 0 ---------------------------------------
     u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
     if (ks.n_tiles > 0) {
-        load_tile<T, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, 0, gk_lds[0]);
+        load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, 0,
+                            gk_lds[0]);
         store_tile<T>(kr, vr, smem);
     }
     __syncthreads();
@@ -207,7 +237,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         const int st = j & 1;
         const bool has_next = j + 1 < ks.n_tiles;
         if (has_next)
-            load_tile<T, GROWS>(kr, vr, kbase, vbase, rowstride, ks, p, j + 1, gk_lds[st ^ 1]);
+            load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, j + 1,
+                                gk_lds[st ^ 1]);
 
         // classify this tile for this wave (wave-uniform)
         const bool band_tile = GROWS || j < ks.n_band_tiles;

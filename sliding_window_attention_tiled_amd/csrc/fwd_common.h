@@ -3,6 +3,8 @@
 // Band work items: (b, kv head, head group, residue class r, position tile).
 // Positions of residue class r are i = r + m*d; a tile is bmq consecutive m.
 // Its key range in residue coordinates is [max(0, m0 - wl), min(Nr-1, m1 + wr)].
+// With a ring (chunked prefill, d = 1, causal) the range starts at
+// max(-cache_len, m0 - wl): coordinate -1 - a is the ring entry of age a.
 // Global-row work items: (b, kv head, head group, row group, key chunk).
 #pragma once
 
@@ -16,6 +18,7 @@ struct KeyStream {
     int n_band_tiles;    // tiles of `tile_keys` keys covering [k_lo, k_hi]
     int n_tiles;         // band tiles plus gathered global-key tiles
     int n_global;
+    int rhead;           // ring: next slot to write (the slot of coordinate 0)
 };
 
 struct WorkItem {
@@ -54,6 +57,13 @@ __device__ __forceinline__ WorkItem decode_band_item(const FwdParams& p, int L, 
     const int m0 = mt * p.bmq;
     const int m_last = min(m0 + p.bmq - 1, w.ks.Nr - 1);
     w.ks.k_lo = max(0, m0 - p.wl);
+    w.ks.rhead = 0;
+    if (p.kring != nullptr) {
+        // ring state is device data: clamp it so that no slot index can leave the ring
+        const int len = min(max(p.cache_len[w.b], 0), p.W);
+        w.ks.rhead = min(max(p.ring_head[w.b], 0), p.W - 1);
+        w.ks.k_lo = max(-len, m0 - p.wl);
+    }
     w.ks.k_hi = min(w.ks.Nr - 1, m_last + p.wr);
     w.ks.n_band_tiles = (w.ks.k_hi - w.ks.k_lo + tile_keys) / tile_keys;
     w.ks.n_global = p.n_global;
@@ -86,8 +96,16 @@ __device__ __forceinline__ WorkItem decode_grows_item(const FwdParams& p, int L,
         w.ks.k_hi >= w.ks.k_lo ? (w.ks.k_hi - w.ks.k_lo + tile_keys) / tile_keys : 0;
     w.ks.n_tiles = w.ks.n_band_tiles;
     w.ks.n_global = p.n_global;
+    w.ks.rhead = 0;
     w.row0 = g_first;
     return w;
+}
+
+// Ring slot of a negative residue coordinate kk (>= -W): the entry of age
+// -1 - kk, written ring_head - 1 - age (mod W).
+__device__ __forceinline__ int ring_slot(const KeyStream& ks, int kk, int W) {
+    const int s = ks.rhead + kk;
+    return s < 0 ? s + W : s;
 }
 
 // Absolute position of key `key` of tile `j`, or -1 when the slot is padding.

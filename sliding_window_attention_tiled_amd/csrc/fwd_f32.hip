@@ -62,16 +62,35 @@ __global__ __launch_bounds__(NT) void swa_fwd_f32_kernel(const FwdParams p) {
     const int rowstride = p.Hkv * D;
     const float* kbase = (const float*)p.k + ((size_t)b * p.N * p.Hkv + kvh) * D;
     const float* vbase = (const float*)p.v + ((size_t)b * p.N * p.Hkv + kvh) * D;
+    // ring rows of this (b, kv head) for chunked prefill (unused otherwise)
+    const size_t ring_off = ((size_t)b * p.Hkv + kvh) * (size_t)p.W * D;
+    const float* krbase = (const float*)p.kring + ring_off;
+    const float* vrbase = (const float*)p.vring + ring_off;
 
     for (int j = 0; j < ks.n_tiles; j++) {
         __syncthreads();  // previous tile fully consumed
         for (int ci = tid; ci < TK * D / 4; ci += NT) {
             const int key = ci / (D / 4), c4 = ci % (D / 4);
-            const int pos = key_position(ks, p, j, key, TK, GROWS);
+            const float* ksrc = nullptr;
+            const float* vsrc = nullptr;
+            const int kk = ks.k_lo + j * TK + key;
+            if (!GROWS && j < ks.n_band_tiles && kk < 0) {
+                // ring entry (chunked prefill)
+                const size_t o = (size_t)ring_slot(ks, kk, p.W) * D + c4 * 4;
+                ksrc = krbase + o;
+                vsrc = vrbase + o;
+            } else {
+                const int pos = key_position(ks, p, j, key, TK, GROWS);
+                if (pos >= 0) {
+                    const size_t o = (size_t)pos * rowstride + c4 * 4;
+                    ksrc = kbase + o;
+                    vsrc = vbase + o;
+                }
+            }
             f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (pos >= 0) {
-                kv = *(const f32x4*)(kbase + (size_t)pos * rowstride + c4 * 4);
-                vv = *(const f32x4*)(vbase + (size_t)pos * rowstride + c4 * 4);
+            if (ksrc != nullptr) {
+                kv = *(const f32x4*)ksrc;
+                vv = *(const f32x4*)vsrc;
             }
             *(f32x4*)(ks_lds + key * PITCH + c4 * 4) = kv;
             *(f32x4*)(vs_lds + key * PITCH + c4 * 4) = vv;

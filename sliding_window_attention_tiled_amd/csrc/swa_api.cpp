@@ -42,6 +42,28 @@ void decode_splits(int B, int Hq, int W, int* splits, int* per_split) {
     *splits = (int)cdiv(W, ps);
 }
 
+// Band work decomposition of a forward launch (p.B, Hkv, group, N, dil set).
+// False when the grid would not fit in 32 bits.
+bool plan_band(FwdParams& p, int dtype, swa::FwdShape* shape_out) {
+    p.qd = p.N / p.dil;
+    p.rem = p.N % p.dil;
+    const swa::FwdShape shape =
+        dtype == SWA_BF16 ? swa::fwd_bf16_shape(p.group) : swa::fwd_f32_shape(p.group);
+    p.hpw = shape.hpw;
+    p.bmq = shape.bmq;
+    p.head_groups = p.group / p.hpw;
+    p.tiles_long = (int)cdiv(p.qd + 1, p.bmq);
+    p.tiles_short = (int)cdiv(p.qd, p.bmq);
+    const int64_t per_slab =
+        (int64_t)p.rem * p.tiles_long + (int64_t)(p.dil - p.rem) * p.tiles_short;
+    const int64_t blocks = (int64_t)p.B * p.Hkv * p.head_groups * per_slab;
+    if (per_slab > INT32_MAX || blocks > INT32_MAX) return false;
+    p.tiles_per_slab = (int)per_slab;
+    p.n_blocks = (int)blocks;
+    *shape_out = shape;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,21 +131,8 @@ int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
     p.wr = std::min(win_right, N);
     p.dil = dilation;
     p.scale_log2 = scale * kLog2e;
-    p.qd = N / dilation;
-    p.rem = N % dilation;
-    const swa::FwdShape shape =
-        dtype == SWA_BF16 ? swa::fwd_bf16_shape(p.group) : swa::fwd_f32_shape(p.group);
-    p.hpw = shape.hpw;
-    p.bmq = shape.bmq;
-    p.head_groups = p.group / p.hpw;
-    p.tiles_long = (int)cdiv(p.qd + 1, p.bmq);
-    p.tiles_short = (int)cdiv(p.qd, p.bmq);
-    const int64_t per_slab =
-        (int64_t)p.rem * p.tiles_long + (int64_t)(dilation - p.rem) * p.tiles_short;
-    const int64_t blocks = (int64_t)B * Hkv * p.head_groups * per_slab;
-    if (per_slab > INT32_MAX || blocks > INT32_MAX) return SWA_ERR_ARG;
-    p.tiles_per_slab = (int)per_slab;
-    p.n_blocks = (int)blocks;
+    swa::FwdShape shape;
+    if (!plan_band(p, dtype, &shape)) return SWA_ERR_ARG;
 
     p.n_global = (int)g.size();
     for (int i = 0; i < p.n_global; i++) p.gpos[i] = g[i];
@@ -161,6 +170,61 @@ int swa_kv_append(void* kcache, void* vcache, const void* k_new, const void* v_n
     const int elem = dtype == SWA_BF16 ? 2 : 4;
     hipError_t e = swa::launch_kv_append(kcache, vcache, k_new, v_new, ring_head, cache_len, B,
                                          Hkv, W, D, elem, stream);
+    return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+}
+
+int swa_kv_append_chunk(void* kcache, void* vcache, const void* k, const void* v,
+                        int32_t* ring_head, int32_t* cache_len, int B, int Hkv, int W, int n,
+                        int D, int dtype, hipStream_t stream) {
+    if (!kcache || !vcache || !ring_head || !cache_len) return SWA_ERR_ARG;
+    if (n > 0 && (!k || !v)) return SWA_ERR_ARG;  // an empty chunk may have no storage
+    if (B <= 0 || Hkv <= 0 || W <= 0 || W > kMaxN || n < 0 || n > kMaxN || D <= 0)
+        return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    if (n == 0) return SWA_OK;
+    const int elem = dtype == SWA_BF16 ? 2 : 4;
+    hipError_t e = swa::launch_kv_append_chunk(kcache, vcache, k, v, ring_head, cache_len, B, Hkv,
+                                               W, n, D, elem, stream);
+    return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+}
+
+int swa_fwd_cached(const void* q, const void* k, const void* v, const void* kcache,
+                   const void* vcache, const int32_t* ring_head, const int32_t* cache_len,
+                   void* out, float* lse, int B, int Hq, int Hkv, int n, int W, int D,
+                   int win_left, float scale, int dtype, hipStream_t stream) {
+    if (!q || !k || !v || !kcache || !vcache || !ring_head || !cache_len || !out)
+        return SWA_ERR_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || n <= 0 || n > kMaxN || W <= 0 || W > kMaxN || D <= 0)
+        return SWA_ERR_ARG;
+    if (Hq % Hkv != 0 || win_left < 0 || win_left > W) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+
+    FwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = n;
+    p.group = Hq / Hkv;
+    p.causal = 1;
+    p.wl = win_left;   // may exceed n: the ring supplies the older keys
+    p.wr = 0;
+    p.dil = 1;
+    p.scale_log2 = scale * kLog2e;
+    p.kring = kcache;
+    p.vring = vcache;
+    p.ring_head = ring_head;
+    p.cache_len = cache_len;
+    p.W = W;
+    swa::FwdShape shape;
+    if (!plan_band(p, dtype, &shape)) return SWA_ERR_ARG;
+    hipError_t e = dtype == SWA_BF16 ? swa::launch_fwd_bf16(p, D, stream)
+                                     : swa::launch_fwd_f32(p, D, stream);
     return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
 }
 

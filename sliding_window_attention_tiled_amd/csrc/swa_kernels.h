@@ -50,6 +50,13 @@ struct FwdParams {
     int g_nchunks;     // splits per global row
     int g_rowgroups;   // workgroups needed to cover n_global rows
     int32_t gpos[SWA_MAX_GLOBAL];
+    // chunked prefill: keys before the chunk come from a ring [B][Hkv][W][D]
+    // (null kring: none).  Residue coordinates -1, -2, ... are ring ages 0, 1, ...
+    const void* kring;
+    const void* vring;
+    const int32_t* ring_head;
+    const int32_t* cache_len;
+    int W;
 };
 
 struct DecodeParams {
@@ -72,7 +79,6 @@ struct CombineParams {
     int rows, splits;
     int mode;               // 0: decode rows (b*Hq + h); 1: global rows of a forward
     int B, Hq, N, n_global;
-    const int32_t* gpos_dev;  // unused (global positions come in gpos below)
     int32_t gpos[SWA_MAX_GLOBAL];
 };
 
@@ -93,6 +99,9 @@ hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn,
                             int32_t* head, int32_t* len, int B, int Hkv, int W, int D,
                             int elem_bytes, hipStream_t s);
+hipError_t launch_kv_append_chunk(void* kc, void* vc, const void* k, const void* v,
+                                  int32_t* head, int32_t* len, int B, int Hkv, int W, int n,
+                                  int D, int elem_bytes, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeParams& p, int D, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, int D, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t s);

@@ -50,4 +50,5 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
         msg += f", rel-rms {rr:.3e}"
         assert rr <= tol["rel_rms"], msg
     assert mx <= tol["max_abs"], msg
+    log("  " + msg)
     return msg

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["swa_fwd", "swa_fwd_workspace_size", "swa_kv_append", "swa_decode",
-              "swa_decode_workspace_size", "swa_status_string", "swa_version"]:
+              "swa_decode_workspace_size", "swa_status_string", "swa_version",
+              "swa_kv_append_chunk", "swa_fwd_cached"]:
         assert n in names
 
 
@@ -134,3 +135,42 @@ def test_python_binding_requires_device_tensors(lib):
     q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(binding.SwaError):
         binding.fwd(q, q, q, win_left=3)
+
+
+def test_kv_append_chunk_validation(lib):
+    f = lib.swa_kv_append_chunk
+    # (kcache, vcache, k, v, head, len, B, Hkv, W, n, D, dtype, stream)
+    assert f(None, P, P, P, P, P, 1, 1, 8, 4, 128, 1, None) == ARG
+    assert f(P, P, None, P, P, P, 1, 1, 8, 4, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, None, 1, 1, 8, 4, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 1, 1, 8, -1, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 1, 1, 0, 4, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 1, 1, 8, (1 << 28) + 1, 128, 1, None) == ARG
+    assert f(P, P, P, P, P, P, 1, 1, 8, 4, 96, 1, None) == UNSUP
+    assert f(P, P, P, P, P, P, 1, 1, 8, 4, 128, 9, None) == UNSUP
+    assert f(P, P, P, P, P, P, 1, 1, 8, 0, 128, 1, None) == OK     # nothing to append
+    assert f(P, P, None, None, P, P, 1, 1, 8, 0, 128, 1, None) == OK
+
+
+def test_fwd_cached_validation(lib):
+    f = lib.swa_fwd_cached
+    names = ["q", "k", "v", "kc", "vc", "head", "len", "out", "lse", "B", "Hq", "Hkv", "n",
+             "W", "D", "wl", "scale", "dtype", "stream"]
+    base = [P, P, P, P, P, P, P, P, None, 1, 8, 2, 64, 128, 128, 127, 0.1, 1, None]
+
+    def call(**ch):
+        a = list(base)
+        for k_, v_ in ch.items():
+            a[names.index(k_)] = v_
+        return f(*a)
+    for ptr in ("q", "k", "v", "kc", "vc", "head", "len", "out"):
+        assert call(**{ptr: None}) == ARG, ptr
+    assert call(B=0) == ARG
+    assert call(n=0) == ARG
+    assert call(W=0) == ARG
+    assert call(Hq=6, Hkv=4) == ARG
+    assert call(wl=-1) == ARG
+    assert call(wl=129) == ARG                                    # window beyond the ring
+    assert call(n=(1 << 28) + 1) == ARG
+    assert call(D=80) == UNSUP
+    assert call(dtype=2) == UNSUP
