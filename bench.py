@@ -9,7 +9,12 @@ fraction uses.  The same JSON line carries the decode leg (64 sequences,
 Hq=32, Hkv=8, D=128, W=4096 ring, append + attend per step) as HBM GB/s of
 K+V streamed, and the fp64 CPU oracle timed on a bounded sample of rows.
 
+Also reported, per call: the bidirectional encoder with global tokens, the
+four layers of the dilated stack and one 4096-token chunk of a chunked prefill
+(exact TFLOP/s against min(MFMA peak, HBM peak x arithmetic intensity)).
+
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
+                    [--no-others]
 """
 from __future__ import annotations
 
@@ -68,8 +73,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the per-call timings of the other workloads")
     ap.add_argument("--cpu-rows", type=int, default=196608)
-    ap.add_argument("--only", choices=["fwd", "decode"], default=None,
+    ap.add_argument("--only", choices=["fwd", "decode", "others"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, the reference "
@@ -191,6 +198,120 @@ def bench_decode(args):
                 step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9)
 
 
+def _time_calls(fn, reps=10, warmup=3):
+    """Mean and min device time (ms) of fn() over reps launches, HIP events on
+    the current stream, after a short clock-settling warm-up."""
+    import torch
+    stream = torch.cuda.current_stream()
+    t_settle = time.perf_counter() + 0.1
+    while time.perf_counter() < t_settle:
+        fn()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(per)), float(np.min(per))
+
+
+def _bound(flop, bytes_):
+    """Roofline bound of a launch: min(MFMA peak, HBM peak x arithmetic intensity)."""
+    return min(PEAK_BF16_TFLOPS, PEAK_HBM_GBS * 1e9 * flop / bytes_ / 1e12)
+
+
+def _report(name, ms, ms_min, flop, bytes_, extra=None):
+    tf = flop / (ms * 1e-3) / 1e12
+    bound = _bound(flop, bytes_)
+    r = {"workload": name, "kernel_ms": round(ms, 4), "kernel_ms_min": round(ms_min, 4),
+         "tflops_exact": round(tf, 2), "bound_tflops": round(bound, 1),
+         "frac_of_bound": round(tf / bound, 4), "algorithmic_bytes": int(bytes_)}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def bench_other_workloads():
+    """The bidirectional encoder with global tokens, the four layers of the
+    dilated stack and one chunk of a chunked prefill, each timed per call and
+    reported as exact TFLOP/s against min(MFMA, HBM x intensity)."""
+    import torch
+    from sliding_window_attention_tiled_amd import binding, configs
+    from sliding_window_attention_tiled_amd.inputs import DecodeInputs, fwd_inputs
+
+    res = []
+    # bidirectional encoder, window 256 + 256, 16 global tokens
+    c = configs.FWD["bidir_encoder_globals"]
+    B, H, N, D = c["B"], c["Hq"], c["N"], c["D"]
+    q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], B, H, H, N, D, c["dtype"]))
+    G = np.array(sorted(set(c["global_idx"])))
+    i = np.arange(N)
+    band = np.minimum(i, c["win_left"]) + np.minimum(N - 1 - i, c["win_right"]) + 1
+    far = ((G[None, :] < i[:, None] - c["win_left"]) |
+           (G[None, :] > i[:, None] + c["win_right"])).sum(1)
+    pairs = np.where(np.isin(i, G), N, band + far).sum()
+    flop = 4.0 * B * H * D * float(pairs)
+    bytes_ = 4.0 * B * N * H * D * 2 + 4.0 * B * H * N
+    ws = torch.empty(binding.fwd_workspace_size(B, H, N, D, len(G)), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ms, mn = _time_calls(lambda: binding.fwd(q, k, v, win_left=c["win_left"],
+                                             win_right=c["win_right"], global_idx=c["global_idx"],
+                                             out=out, lse=lse, workspace=ws))
+    res.append(_report("bidir_encoder_globals", ms, mn, flop, bytes_))
+    del q, k, v, out, lse, ws
+
+    # dilated stack: one call per dilation on the same q/k/v
+    c = configs.DILATED_STACK
+    B, H, N, D = c["B"], c["Hq"], c["N"], c["D"]
+    q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], B, H, H, N, D, c["dtype"]))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    bytes_ = 4.0 * B * N * H * D * 2 + 4.0 * B * H * N
+    for d in c["dilations"]:
+        # causal dilated band: i, i - d, ..., down to max(i - wl*d, i mod d)
+        pairs = (np.minimum(c["win_left"], np.arange(N) // d) + 1).sum()
+        flop = 4.0 * B * H * D * float(pairs)
+        ms, mn = _time_calls(lambda: binding.fwd(q, k, v, win_left=c["win_left"], win_right=0,
+                                                 dilation=d, out=out, lse=lse))
+        res.append(_report(f"dilated_stack_d{d}", ms, mn, flop, bytes_))
+    del q, k, v, out, lse
+
+    # chunked prefill: a 4096-token chunk after a full 4096-slot ring
+    c = configs.PREFILL_CHUNK
+    B, Hq, Hkv, W, D, n = c["B"], c["Hq"], c["Hkv"], c["W"], c["D"], c["chunk"]
+    gen = DecodeInputs(c["seed"], B, Hq, Hkv, W, D, c["dtype"])
+    q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"] + 100, B, Hq, Hkv, n, D, c["dtype"]))
+    kc, vc = to_dev(gen.kcache), to_dev(gen.vcache)
+    head = torch.from_numpy(gen.ring_head.copy()).to("cuda")
+    length = torch.from_numpy(gen.cache_len.copy()).to("cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
+    t = np.arange(n)
+    wl = c["win_left"]
+    pairs = (np.minimum(W, np.maximum(wl - t, 0)) + np.minimum(t, wl) + 1).sum()
+    flop = 4.0 * B * Hq * D * float(pairs)
+    bytes_ = (2.0 * B * n * Hq * D * 2 + 2.0 * B * n * Hkv * D * 2 + 2.0 * B * Hkv * W * D * 2
+              + 4.0 * B * Hq * n)
+    ms, mn = _time_calls(lambda: binding.fwd_cached(q, k, v, kc, vc, head, length,
+                                                    win_left=wl, out=out, lse=lse))
+    # the hand-off copy of the chunk into a scratch ring (state restored each time)
+    kc2, vc2 = kc.clone(), vc.clone()
+    h2, l2 = head.clone(), length.clone()
+    ams, amn = _time_calls(lambda: binding.kv_append_chunk(kc2, vc2, k, v, h2, l2))
+    append_bytes = 2.0 * 2 * B * min(n, W) * Hkv * D * 2   # read chunk + write ring, K and V
+    res.append(_report("prefill_chunk4096_after_full_ring", ms, mn, flop, bytes_,
+                       {"append_chunk_ms": round(ams, 4),
+                        "append_chunk_gbs": round(append_bytes / (ams * 1e-3) / 1e9, 1)}))
+    return res
+
+
 def cpu_baseline(inputs, cfg, n_rows):
     import oracle
 
@@ -228,6 +349,9 @@ def main():
     if args.only == "decode":
         print(json.dumps({"decode": bench_decode(args)}))
         return
+    if args.only == "others":
+        print(json.dumps({"other_workloads": bench_other_workloads()}))
+        return
     f = bench_fwd(args)
     ms = f["ms_kernel"]
     value = f["nominal_flop"] / (ms * 1e-3) / 1e12
@@ -255,6 +379,8 @@ def main():
     }
     if not args.no_decode and args.only is None:
         res["decode"] = bench_decode(args)
+    if not args.no_others and args.only is None:
+        res["other_workloads"] = bench_other_workloads()
     if not args.no_cpu and args.only is None:
         res["cpu_baseline"] = cpu_baseline(f["inputs"], f["cfg"], args.cpu_rows)
     print(json.dumps(res))

@@ -28,9 +28,17 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
     return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
-__device__ __forceinline__ float wave_max_xor32(float x) {
-    return fmaxf(x, __shfl_xor(x, 32));
+// Value of lane l ^ 32, on the vector ALU (v_permlane32_swap exchanges the
+// two 32-lane halves; no LDS round trip).  Whether the compiler swaps one
+// register in place or two copies, lane l < 32 finds its partner in the
+// second result and lane l >= 32 in the first.
+__device__ __forceinline__ float lane_xor32(float x) {
+    const unsigned b = __builtin_bit_cast(unsigned, x);
+    const auto sw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (threadIdx.x & 32) ? sw[0] : sw[1]);
 }
+
+__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, lane_xor32(x)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

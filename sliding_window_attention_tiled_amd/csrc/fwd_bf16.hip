@@ -79,7 +79,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
                                           const __bf16* kbase, const __bf16* vbase,
                                           const __bf16* krbase, const __bf16* vrbase,
                                           int rowstride, const KeyStream& ks, const FwdParams& p,
-                                          int j, int* gk) {
+                                          int j, int* gk, const int* gpos) {
     const int key0 = threadIdx.x / T::CPR;
     const int c = threadIdx.x % T::CPR;
     if (!GROWS && j < ks.n_band_tiles && ks.k_lo + j * BN < 0) {
@@ -117,7 +117,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
 #pragma unroll
         for (int u = 0; u < T::PER_THREAD; u++) {
             const int gi = g0 + u * T::KEY_STEP;
-            kpos[u] = gi < ks.n_global ? p.gpos[gi] : -1;
+            kpos[u] = gi < ks.n_global ? gpos[gi] : -1;
             if (c == 0) {
                 const int g = kpos[u];
                 gk[key0 + u * T::KEY_STEP] = g;
@@ -164,6 +164,10 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
 
     __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::STAGE];
     __shared__ __attribute__((aligned(16))) int gk_lds[2][2 * BN];
+    // the global positions, read by the gathered-key tile loads.  Kept in LDS:
+    // a per-lane load from the parameter block inside the tile loop would be a
+    // vector-memory write that the compiler waits for before the next LDS read.
+    __shared__ int gpos_lds[SWA_MAX_GLOBAL];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -225,10 +229,14 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     const bf16x2 ones = {one, one};
 
     // ---- prologue: tile 0 into stage 0 ---------------------------------------
+    // (tile 0 is a band tile: the barrier below publishes gpos_lds before the
+    // first gathered-key tile is loaded)
+    if (!GROWS)
+        for (int i = threadIdx.x; i < p.n_global; i += T::NT) gpos_lds[i] = p.gpos[i];
     u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
     if (ks.n_tiles > 0) {
         load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, 0,
-                            gk_lds[0]);
+                            gk_lds[0], gpos_lds);
         store_tile<T>(kr, vr, smem);
     }
     __syncthreads();
@@ -236,9 +244,6 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     for (int j = 0; j < ks.n_tiles; j++) {
         const int st = j & 1;
         const bool has_next = j + 1 < ks.n_tiles;
-        if (has_next)
-            load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, j + 1,
-                                gk_lds[st ^ 1]);
 
         // classify this tile for this wave (wave-uniform)
         const bool band_tile = GROWS || j < ks.n_band_tiles;
@@ -249,11 +254,12 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             skip = w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl;
             need_mask = !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
         }
+        const unsigned short* Ks = smem + st * T::STAGE;
+        const unsigned short* Vs = Ks + T::K_ELEMS;
+        f32x16 s[QB][2];
+        float m_use[QB];
         if (!skip) {
-            const unsigned short* Ks = smem + st * T::STAGE;
-            const unsigned short* Vs = Ks + T::K_ELEMS;
             // S^T = K Q^T : two 32-key blocks x QB 32-query blocks
-            f32x16 s[QB][2];
 #pragma unroll
             for (int qb = 0; qb < QB; qb++) {
                 s[qb][0] = f32x16{};
@@ -281,6 +287,15 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 __builtin_amdgcn_sched_group_barrier(0x100, KBATCH, 0);       // DS reads first
                 __builtin_amdgcn_sched_group_barrier(0x008, KBATCH * QB, 0);  // then MFMAs
             }
+        }
+        // Next tile into registers, issued after the score MFMAs: a load issued
+        // before them makes the compiler wait for it ahead of the first MFMA
+        // (their results may reuse the loads' address registers).  The loads
+        // then overlap the softmax and P V, and are stored after them.
+        if (has_next)
+            load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, j + 1,
+                                gk_lds[st ^ 1], gpos_lds);
+        if (!skip) {
             // Element masks.  Lane key offsets within the tile are
             // kb*32 + (e>>2)*8 + half*4 + (e&3); all compares are per element.
             if (need_mask) {
@@ -351,7 +366,6 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             }
             // online softmax: running max first, then per 16-key step the bf16
             // weights (B operand of P V) and their sum
-            float m_use[QB];
 #pragma unroll
             for (int qb = 0; qb < QB; qb++) {
                 float mx = s[qb][0][0];
@@ -416,7 +430,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     // ---- epilogue ---------------------------------------------------------------
 #pragma unroll
     for (int qb = 0; qb < QB; qb++) {
-        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+        const float l_tot = l_run[qb] + lane_xor32(l_run[qb]);
         if (qpos[qb] < 0) continue;
         if (!GROWS) {
             const float inv = 1.0f / l_tot;
