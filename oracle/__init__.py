@@ -85,6 +85,9 @@ class OracleLib:
         lib.oracle_fwd_cached.argtypes = [P, P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I64,
                                           I64, D, P, P]
         lib.oracle_fwd_cached.restype = I
+        lib.oracle_decode_sinks.argtypes = [P, P, P, P, P, I64, I, P, P, I64, I64, I64, I64,
+                                            I64, D, P, P]
+        lib.oracle_decode_sinks.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         self.lib = lib
@@ -207,14 +210,26 @@ class Ring:
             raise ValueError("invalid arguments to oracle_fwd_cached")
         return out, lse
 
-    def decode(self, q, scale=None):
-        """q [B,Hq,D] -> (out [B,Hq,D], lse [B,Hq]) fp64."""
+    def decode(self, q, scale=None, sinks=None):
+        """q [B,Hq,D] -> (out [B,Hq,D], lse [B,Hq]) fp64.  sinks = (ksink, vsink)
+        [B,Hkv,S,D]: pinned entries attended in addition to the ring."""
         q, _ = _as_input(q)
         B, Hq, D = q.shape
         if scale is None:
             scale = 1.0 / np.sqrt(D)
         out = np.zeros((B, Hq, D), np.float64)
         lse = np.zeros((B, Hq), np.float64)
+        if sinks is not None:
+            ks, _ = _as_input(sinks[0])
+            vs, _ = _as_input(sinks[1])
+            rc = self.orc.lib.oracle_decode_sinks(_ptr(q), _ptr(self.k), _ptr(self.v), _ptr(ks),
+                                                  _ptr(vs), ks.shape[2], self.dtype,
+                                                  _ptr(self.head), _ptr(self.len), B, Hq,
+                                                  self.Hkv, self.W, D, float(scale), _ptr(out),
+                                                  _ptr(lse))
+            if rc != 0:
+                raise ValueError("invalid arguments to oracle_decode_sinks")
+            return out, lse
         rc = self.orc.lib.oracle_decode(_ptr(q), _ptr(self.k), _ptr(self.v), self.dtype,
                                         _ptr(self.head), _ptr(self.len), B, Hq, self.Hkv,
                                         self.W, D, float(scale), _ptr(out), _ptr(lse))

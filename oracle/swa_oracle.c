@@ -405,6 +405,70 @@ int oracle_fwd_cached(const void* q, const void* k, const void* v, const void* k
     return 0;
 }
 
+/* ---- decode with attention-sink slots ------------------------------------ */
+
+/* One decode step over the ring plus n_sink pinned entries (mhpn.cn "Dilated
+ * sliding window", section 3: keep the first tokens as attention-sink anchors;
+ * aiqz.cc "global attention tokens": some tokens stay visible to every later
+ * token).  ksink, vsink [B,Hkv,n_sink,D] hold the first n_sink tokens of each
+ * sequence, which never enter the ring (it holds the tokens after them) and
+ * are never evicted.  Query (b, h) attends the cache_len[b] valid ring slots
+ * and all n_sink sink entries.  out [B,Hq,D], lse [B,Hq] in double.  A row with
+ * no key at all (cache_len == 0 and n_sink == 0) is an error (-1). */
+int oracle_decode_sinks(const void* q, const void* kcache, const void* vcache,
+                        const void* ksink, const void* vsink, int64_t n_sink, int dtype,
+                        const int64_t* ring_head, const int64_t* cache_len, int64_t B,
+                        int64_t Hq, int64_t Hkv, int64_t W, int64_t D, double scale,
+                        double* out, double* lse) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || D <= 0 || n_sink < 0 ||
+        (dtype != 0 && dtype != 1))
+        return -1;
+    for (int64_t b = 0; b < B; b++)
+        if (ring_head[b] < 0 || ring_head[b] >= W || cache_len[b] < 0 || cache_len[b] > W ||
+            cache_len[b] + n_sink < 1)
+            return -1;
+    const int64_t group = Hq / Hkv;
+    const int64_t cap = W + n_sink;
+    const size_t esz = dtype == 0 ? 4 : 2;
+#pragma omp parallel
+    {
+        void* kt = malloc(esz * (size_t)(cap * D));
+        void* vt = malloc(esz * (size_t)(cap * D));
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+        double* s = (double*)malloc(sizeof(double) * (size_t)cap);
+        for (int64_t t = 0; t < cap; t++) keys[t] = t;
+#pragma omp for schedule(static)
+        for (int64_t bh = 0; bh < B * Hq; bh++) {
+            int64_t nk = 0;
+            const int64_t b = bh / Hq, kh = (bh % Hq) / group;
+            for (int64_t t = 0; t < n_sink; t++) { /* the pinned entries */
+                const int64_t base = ((b * Hkv + kh) * n_sink + t) * D;
+                for (int64_t c = 0; c < D; c++) {
+                    copy_elem(kt, ksink, dtype, nk * D + c, base + c);
+                    copy_elem(vt, vsink, dtype, nk * D + c, base + c);
+                }
+                nk++;
+            }
+            for (int64_t a = 0; a < cache_len[b]; a++) { /* the valid ring slots */
+                const int64_t slot = ((ring_head[b] - 1 - a) % W + W) % W;
+                const int64_t base = ((b * Hkv + kh) * W + slot) * D;
+                for (int64_t c = 0; c < D; c++) {
+                    copy_elem(kt, kcache, dtype, nk * D + c, base + c);
+                    copy_elem(vt, vcache, dtype, nk * D + c, base + c);
+                }
+                nk++;
+            }
+            attend_row(q, bh * D, kt, vt, 0, D, dtype, D, keys, nk, scale, s, out + bh * D,
+                       lse + bh);
+        }
+        free(kt);
+        free(vt);
+        free(keys);
+        free(s);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

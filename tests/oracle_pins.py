@@ -407,9 +407,45 @@ def pin_prefill_then_decode(orc):
         _close(l, ref_l[:, :, t], 1e-12, f"decode lse at {t}")
 
 
+def pin_decode_sinks(orc):
+    """Decode with the first S tokens pinned as sinks (the ring holding the
+    tokens after them) equals the causal window-W forward with global tokens
+    0..S-1 at every decode row (dense-mask brute force); q = 0 gives the mean
+    over sinks and held ring entries; no sinks is plain decode."""
+    B, Hq, Hkv, D, W, S = 2, 4, 2, 8, 6, 3
+    N = 20
+    q, k, v = fwd_inputs(320, B, Hq, Hkv, N, D, "bf16")
+    ref_o, ref_l = bruteforce.fwd(q, k, v, win_left=W - 1, win_right=0,
+                                  global_idx=list(range(S)), scale=0.35)
+    ks = np.ascontiguousarray(k[:, :S].transpose(0, 2, 1, 3))
+    vs = np.ascontiguousarray(v[:, :S].transpose(0, 2, 1, 3))
+    ring = _empty_ring(orc, B, Hkv, W, D, "bf16", [2, 5])
+    for t in range(S, N):
+        ring.append(np.ascontiguousarray(k[:, t]), np.ascontiguousarray(v[:, t]))
+        o, l = ring.decode(np.ascontiguousarray(q[:, t]), scale=0.35, sinks=(ks, vs))
+        _close(o, ref_o[:, t], 1e-12, f"decode with sinks at {t}")
+        _close(l, ref_l[:, :, t], 1e-12, f"decode with sinks lse at {t}")
+    # q = 0: uniform weights over sinks and the held ring entries
+    o, l = ring.decode(np.zeros((B, Hq, D), np.uint16), scale=1.0, sinks=(ks, vs))
+    for b in range(B):
+        held = [(int(ring.head[b]) - 1 - a) % W for a in range(int(ring.len[b]))]
+        vals = np.concatenate([bruteforce.widen(vs[b]), bruteforce.widen(ring.v[b][:, held])],
+                              axis=1)                         # [Hkv, S + len, D]
+        for h in range(Hq):
+            _close(o[b, h], vals[h // (Hq // Hkv)].mean(axis=0), 1e-12, "sinks q=0 mean")
+        _close(l[b], math.log(vals.shape[1]), 1e-12, "sinks q=0 lse")
+    # no sinks: the plain decode
+    z = np.zeros((B, Hkv, 0, D), np.uint16)
+    qd = np.ascontiguousarray(q[:, N - 1])
+    o1, l1 = ring.decode(qd, scale=0.35, sinks=(z, z))
+    o2, l2 = ring.decode(qd, scale=0.35)
+    _close(o1, o2, 0.0, "zero sinks out")
+    _close(l1, l2, 0.0, "zero sinks lse")
+
+
 ALL_PINS = [
     pin_dilated_index_sets, pin_dilated_span, pin_edge_truncation, pin_decode_demo_window,
     pin_ring_buffer_trace, pin_bruteforce, pin_bruteforce_mask_is_page_mask, pin_full_window,
     pin_zero_window, pin_q_zero, pin_dilation_strided, pin_gqa, pin_globals, pin_decode,
-    pin_append_chunk, pin_chunked_prefill, pin_prefill_then_decode,
+    pin_append_chunk, pin_chunked_prefill, pin_prefill_then_decode, pin_decode_sinks,
 ]

@@ -61,6 +61,11 @@ MUTATIONS = {
                                   "ring_head[b] = (ring_head[b] + (n < W ? n : W)) % W;"),
     "chunk_len_uncapped": ("cache_len[b] = cache_len[b] + n < W ? cache_len[b] + n : W;",
                            "cache_len[b] = cache_len[b] + n;"),
+    "sinks_skipped": ("for (int64_t t = 0; t < n_sink; t++) { /* the pinned entries */",
+                      "for (int64_t t = 1; t < n_sink; t++) { /* the pinned entries */"),
+    "sinks_kv_head_modulo": ("kh = (bh % Hq) / group;", "kh = (bh % Hq) % Hkv;"),
+    "sinks_ring_oldest_dropped": ("for (int64_t a = 0; a < cache_len[b]; a++) { /* the valid",
+                                  "for (int64_t a = 0; a + 1 < cache_len[b]; a++) { /* the valid"),
 }
 
 
