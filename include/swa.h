@@ -223,6 +223,40 @@ int swa_decode(const void* q, const void* kcache, const void* vcache,
 /* Bytes of device workspace swa_decode needs for these sizes (0 on bad sizes). */
 size_t swa_decode_workspace_size(int B, int Hq, int W, int D);
 
+/*
+ * swa_decode_sinks: swa_decode plus n_sink attention-sink entries that stay
+ * visible to every step and are never evicted (mhpn.cn "Dilated sliding
+ * window", section 3: the first tokens kept as attention-sink anchors; aiqz.cc,
+ * "global attention tokens").  The sink buffers hold the first n_sink tokens
+ * of each sequence; those tokens do not enter the ring, which holds the tokens
+ * after them.  Each query attends the valid ring slots and all sink entries;
+ * the result equals the causal window-W forward with global positions
+ * 0..n_sink-1 at the decode row (W = ring size, window W keys).
+ *
+ *   ksink, vsink  device, [B, Hkv, n_sink, D] of `dtype` (read only); may be
+ *                 NULL when n_sink == 0.  Filling them: swa_kv_append_chunk on
+ *                 a ring of n_sink slots starting at ring_head = cache_len = 0
+ *                 puts token t of the chunk in slot t.
+ *   n_sink        0 <= n_sink <= SWA_MAX_N; the sink entries form one extra
+ *                 split per (b, kv head), so they should stay few next to W.
+ *   workspace     at least swa_decode_sinks_workspace_size(B, Hq, W, D, n_sink)
+ *                 bytes.
+ *   Everything else as for swa_decode (which is this call with n_sink == 0).
+ *   A sequence with cache_len == 0 and n_sink == 0 gets out = 0, lse = -inf.
+ *
+ * Errors: as swa_decode, plus SWA_ERR_ARG for n_sink < 0, n_sink > SWA_MAX_N
+ * or NULL sink buffers with n_sink > 0.
+ */
+int swa_decode_sinks(const void* q, const void* kcache, const void* vcache,
+                     const int32_t* ring_head, const int32_t* cache_len,
+                     const void* ksink, const void* vsink, int n_sink,
+                     void* out, float* lse,
+                     int B, int Hq, int Hkv, int W, int D, float scale,
+                     void* workspace, size_t workspace_bytes, int dtype, hipStream_t stream);
+
+/* Bytes of device workspace swa_decode_sinks needs (0 on bad sizes). */
+size_t swa_decode_sinks_workspace_size(int B, int Hq, int W, int D, int n_sink);
+
 /* A static, human-readable description of a status code. */
 const char* swa_status_string(int status);
 

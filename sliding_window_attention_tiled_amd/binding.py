@@ -51,6 +51,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swa_fwd_cached.restype = I
     lib.swa_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, P, SZ, I, P]
     lib.swa_decode.restype = I
+    lib.swa_decode_sinks.argtypes = [P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, F, P, SZ,
+                                     I, P]
+    lib.swa_decode_sinks.restype = I
+    lib.swa_decode_sinks_workspace_size.argtypes = [I, I, I, I, I]
+    lib.swa_decode_sinks_workspace_size.restype = SZ
     lib.swa_decode_workspace_size.argtypes = [I, I, I, I]
     lib.swa_decode_workspace_size.restype = SZ
     lib.swa_status_string.argtypes = [I]
@@ -240,4 +245,47 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                         _dtype_code(q), _stream(q))
     _check(st, "swa_decode")
+    return (out, lse) if return_lse else out
+
+
+def decode_sinks_workspace_size(B: int, Hq: int, W: int, D: int, n_sink: int) -> int:
+    return int(load_library().swa_decode_sinks_workspace_size(B, Hq, W, D, n_sink))
+
+
+def decode_sinks(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                 ring_head: torch.Tensor, cache_len: torch.Tensor, ksink: torch.Tensor,
+                 vsink: torch.Tensor, *, scale: float | None = None,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, return_lse: bool = True):
+    """One decode step over the ring and the sink entries ksink/vsink [B,Hkv,S,D]."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, W = kcache.shape[1], kcache.shape[2]
+    S = ksink.shape[2]
+    if kcache.shape != (B, Hkv, W, D) or vcache.shape != kcache.shape:
+        raise SwaError(-1, "decode_sinks ring shape mismatch")
+    if ksink.shape != (B, Hkv, S, D) or vsink.shape != ksink.shape:
+        raise SwaError(-1, "decode_sinks sink shape mismatch")
+    for t in (kcache, vcache, ksink, vsink):
+        if t.dtype != q.dtype:
+            raise SwaError(-1, "q, the ring and the sinks must share one dtype")
+    _ring_state(ring_head, cache_len, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_sinks_workspace_size(B, Hq, W, D, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.swa_decode_sinks(_dev(q, "q"), _dev(kcache, "kcache"), _dev(vcache, "vcache"),
+                              _dev(ring_head, "ring_head"), _dev(cache_len, "cache_len"),
+                              _dev(ksink, "ksink") if S else None,
+                              _dev(vsink, "vsink") if S else None, S,
+                              _dev(out, "out"), _dev(lse, "lse"), B, Hq, Hkv, W, D,
+                              float(scale), _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _dtype_code(q),
+                              _stream(q))
+    _check(st, "swa_decode_sinks")
     return (out, lse) if return_lse else out

@@ -116,14 +116,17 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     const bool head_ok = head_col < p.group;
     const int hq = kvh * p.group + head_col;
 
+    // the last split (when there are sinks) walks the sink entries, all valid
+    const bool sink_split = s >= p.ring_splits;
     const int W = p.W;
     const int ring_head = p.ring_head[b];
     const int cache_len = p.cache_len[b];
-    const bool full = cache_len >= W;
+    const bool full = sink_split || cache_len >= W;
+    const int src_slots = sink_split ? p.n_sink : W;
 
     // slots of this wave
-    const int s_lo = s * p.slots_per_split;
-    const int s_hi = min(W, s_lo + p.slots_per_split);
+    const int s_lo = sink_split ? 0 : s * p.slots_per_split;
+    const int s_hi = sink_split ? p.n_sink : min(W, s_lo + p.slots_per_split);
     const int per_wave = (s_hi - s_lo + 3) / 4;
     const int w_lo = min(s_hi, s_lo + wave * per_wave);
     const int w_hi = min(s_hi, w_lo + per_wave);
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             qreg[k] = head_ok ? *(const bf16x8*)(qp + k * 32)
                               : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    const size_t slab = ((size_t)b * p.Hkv + kvh) * W;
-    const __bf16* kbase = (const __bf16*)p.kcache + slab * D;
-    const __bf16* vbase = (const __bf16*)p.vcache + slab * D;
+    const size_t slab = ((size_t)b * p.Hkv + kvh) * src_slots;
+    const __bf16* kbase = (const __bf16*)(sink_split ? p.ksink : p.kcache) + slab * D;
+    const __bf16* vbase = (const __bf16*)(sink_split ? p.vsink : p.vcache) + slab * D;
     unsigned short* Ks = smem + wave * C::WAVE_ELEMS;
     unsigned short* Vs = Ks + CH * C::PITCH;
 
@@ -296,17 +299,21 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
     const int hq = L % p.Hq;
     const int b = L / p.Hq;
     const int kvh = hq / p.group;
+    const bool sink_split = s >= p.ring_splits;  // sink entries: all valid
     const int W = p.W;
-    const int ring_head = p.ring_head[b], cache_len = p.cache_len[b];
-    const int s_lo = s * p.slots_per_split, s_hi = min(W, s_lo + p.slots_per_split);
+    const int ring_head = p.ring_head[b];
+    const int cache_len = sink_split ? W : p.cache_len[b];
+    const int src_slots = sink_split ? p.n_sink : W;
+    const int s_lo = sink_split ? 0 : s * p.slots_per_split;
+    const int s_hi = sink_split ? p.n_sink : min(W, s_lo + p.slots_per_split);
 
     float q[DL];
     const float* qp = (const float*)p.q + ((size_t)b * p.Hq + hq) * D + part * DL;
 #pragma unroll
     for (int d = 0; d < DL; d++) q[d] = qp[d];
-    const size_t slab = ((size_t)b * p.Hkv + kvh) * W;
-    const float* kbase = (const float*)p.kcache + slab * D + part * DL;
-    const float* vbase = (const float*)p.vcache + slab * D + part * DL;
+    const size_t slab = ((size_t)b * p.Hkv + kvh) * src_slots;
+    const float* kbase = (const float*)(sink_split ? p.ksink : p.kcache) + slab * D + part * DL;
+    const float* vbase = (const float*)(sink_split ? p.vsink : p.vcache) + slab * D + part * DL;
     float acc[DL];
 #pragma unroll
     for (int d = 0; d < DL; d++) acc[d] = 0.f;

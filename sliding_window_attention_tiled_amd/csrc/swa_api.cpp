@@ -228,21 +228,28 @@ int swa_fwd_cached(const void* q, const void* k, const void* v, const void* kcac
     return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
 }
 
-size_t swa_decode_workspace_size(int B, int Hq, int W, int D) {
-    if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(D)) return 0;
+size_t swa_decode_sinks_workspace_size(int B, int Hq, int W, int D, int n_sink) {
+    if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(D) || n_sink < 0) return 0;
     int splits, per;
     decode_splits(B, Hq, W, &splits, &per);
+    splits += n_sink > 0 ? 1 : 0;  // the sink entries get a split of their own
     return (size_t)B * Hq * splits * swa::partial_floats(D) * sizeof(float);
 }
 
-int swa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ring_head,
-               const int32_t* cache_len, void* out, float* lse, int B, int Hq, int Hkv, int W,
-               int D, float scale, void* workspace, size_t workspace_bytes, int dtype,
-               hipStream_t stream) {
+size_t swa_decode_workspace_size(int B, int Hq, int W, int D) {
+    return swa_decode_sinks_workspace_size(B, Hq, W, D, 0);
+}
+
+int swa_decode_sinks(const void* q, const void* kcache, const void* vcache,
+                     const int32_t* ring_head, const int32_t* cache_len, const void* ksink,
+                     const void* vsink, int n_sink, void* out, float* lse, int B, int Hq,
+                     int Hkv, int W, int D, float scale, void* workspace,
+                     size_t workspace_bytes, int dtype, hipStream_t stream) {
     if (!q || !kcache || !vcache || !ring_head || !cache_len || !out) return SWA_ERR_ARG;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0 || D <= 0 || Hq % Hkv != 0) return SWA_ERR_ARG;
+    if (n_sink < 0 || n_sink > kMaxN || (n_sink > 0 && (!ksink || !vsink))) return SWA_ERR_ARG;
     if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < swa_decode_workspace_size(B, Hq, W, D))
+    if (!workspace || workspace_bytes < swa_decode_sinks_workspace_size(B, Hq, W, D, n_sink))
         return SWA_ERR_WORKSPACE;
     DecodeParams p;
     std::memset(&p, 0, sizeof p);
@@ -258,7 +265,11 @@ int swa_decode(const void* q, const void* kcache, const void* vcache, const int3
     p.W = W;
     p.group = Hq / Hkv;
     p.scale_log2 = scale * kLog2e;
-    decode_splits(B, Hq, W, &p.splits, &p.slots_per_split);
+    decode_splits(B, Hq, W, &p.ring_splits, &p.slots_per_split);
+    p.ksink = ksink;
+    p.vsink = vsink;
+    p.n_sink = n_sink;
+    p.splits = p.ring_splits + (n_sink > 0 ? 1 : 0);
     hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, stream)
                                      : swa::launch_decode_f32(p, D, stream);
     if (e != hipSuccess) return SWA_ERR_HIP;
@@ -274,6 +285,15 @@ int swa_decode(const void* q, const void* kcache, const void* vcache, const int3
     c.Hq = Hq;
     if (swa::launch_combine(c, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
     return SWA_OK;
+}
+
+int swa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ring_head,
+               const int32_t* cache_len, void* out, float* lse, int B, int Hq, int Hkv, int W,
+               int D, float scale, void* workspace, size_t workspace_bytes, int dtype,
+               hipStream_t stream) {
+    return swa_decode_sinks(q, kcache, vcache, ring_head, cache_len, nullptr, nullptr, 0, out,
+                            lse, B, Hq, Hkv, W, D, scale, workspace, workspace_bytes, dtype,
+                            stream);
 }
 
 }  // extern "C"

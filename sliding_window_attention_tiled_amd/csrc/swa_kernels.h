@@ -67,9 +67,14 @@ struct DecodeParams {
     const int32_t* cache_len;
     float* partials;   // [B][Hq][splits][D+4]
     int B, Hq, Hkv, W, group;
-    int splits;        // workgroups per (b, kv head)
+    int splits;        // partials per row: ring splits, plus one for the sinks
+    int ring_splits;   // splits over the ring's W slots
     int slots_per_split;
     float scale_log2;
+    // attention-sink entries [B][Hkv][n_sink][D] beside the ring (n_sink = 0: none)
+    const void* ksink;
+    const void* vsink;
+    int n_sink;
 };
 
 struct CombineParams {

@@ -32,7 +32,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["swa_fwd", "swa_fwd_workspace_size", "swa_kv_append", "swa_decode",
               "swa_decode_workspace_size", "swa_status_string", "swa_version",
-              "swa_kv_append_chunk", "swa_fwd_cached"]:
+              "swa_kv_append_chunk", "swa_fwd_cached", "swa_decode_sinks",
+              "swa_decode_sinks_workspace_size"]:
         assert n in names
 
 
@@ -174,3 +175,30 @@ def test_fwd_cached_validation(lib):
     assert call(n=(1 << 28) + 1) == ARG
     assert call(D=80) == UNSUP
     assert call(dtype=2) == UNSUP
+
+
+def test_decode_sinks_validation(lib):
+    f = lib.swa_decode_sinks
+    need = lib.swa_decode_sinks_workspace_size(2, 8, 64, 128, 4)
+    assert need > lib.swa_decode_workspace_size(2, 8, 64, 128)      # one more split
+    assert lib.swa_decode_sinks_workspace_size(2, 8, 64, 128, 0) == \
+        lib.swa_decode_workspace_size(2, 8, 64, 128)
+    assert lib.swa_decode_sinks_workspace_size(2, 8, 64, 128, -1) == 0
+    names = ["q", "kc", "vc", "head", "len", "ks", "vs", "ns", "out", "lse", "B", "Hq", "Hkv",
+             "W", "D", "scale", "ws", "wsb", "dtype", "stream"]
+    base = [P, P, P, P, P, P, P, 4, P, None, 2, 8, 2, 64, 128, 0.1, P, need, 1, None]
+
+    def call(**ch):
+        a = list(base)
+        for k_, v_ in ch.items():
+            a[names.index(k_)] = v_
+        return f(*a)
+    assert call(ks=None) == ARG
+    assert call(vs=None) == ARG
+    assert call(ns=-1) == ARG
+    assert call(ns=(1 << 28) + 1) == ARG
+    assert call(q=None) == ARG
+    assert call(Hq=6, Hkv=4) == ARG
+    assert call(D=80) == UNSUP
+    assert call(wsb=need - 4) == WS
+    assert call(ws=None) == WS
