@@ -88,6 +88,12 @@ class OracleLib:
         lib.oracle_decode_sinks.argtypes = [P, P, P, P, P, I64, I, P, P, I64, I64, I64, I64,
                                             I64, D, P, P]
         lib.oracle_decode_sinks.restype = I
+        lib.oracle_kv_append_paged.argtypes = [P, P, P, P, P, I64, I64, I64, P, I64, I64, I64,
+                                               I64, I64, I]
+        lib.oracle_kv_append_paged.restype = I
+        lib.oracle_decode_paged.argtypes = [P, P, P, I, P, I64, I64, I64, P, I64, I64, I64, I64,
+                                            I64, D, P, P]
+        lib.oracle_decode_paged.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         self.lib = lib
@@ -154,6 +160,9 @@ class OracleLib:
 
     def ring(self, kcache, vcache, ring_head, cache_len) -> "Ring":
         return Ring(self, kcache, vcache, ring_head, cache_len)
+
+    def paged(self, kpool, vpool, seq_len, W: int) -> "PagedCache":
+        return PagedCache(self, kpool, vpool, seq_len, W)
 
 
 class Ring:
@@ -238,6 +247,49 @@ class Ring:
         return out, lse
 
 
+class PagedCache:
+    """The oracle's copy of a paged window cache: page pool kpool/vpool
+    [n_pages,Hkv,P,D], per-sequence token counts seq_len [B] and window W.
+    The block table [B,nb] (int32) is passed to each call."""
+
+    def __init__(self, orc: OracleLib, kpool, vpool, seq_len, W: int):
+        self.orc = orc
+        self.k, self.dtype = _as_input(np.array(kpool, copy=True))
+        self.v, _ = _as_input(np.array(vpool, copy=True))
+        self.len = np.ascontiguousarray(np.asarray(seq_len, dtype=np.int64).copy())
+        self.n_pages, self.Hkv, self.P, self.D = self.k.shape
+        self.W = W
+
+    def append(self, k, v, block_table):
+        """k, v [B,n,Hkv,D]."""
+        k, _ = _as_input(k)
+        v, _ = _as_input(v)
+        bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+        B, n = k.shape[0], k.shape[1]
+        rc = self.orc.lib.oracle_kv_append_paged(_ptr(self.k), _ptr(self.v), _ptr(k), _ptr(v),
+                                                 _ptr(bt), bt.shape[1], self.P, self.n_pages,
+                                                 _ptr(self.len), B, self.Hkv, self.W, n, self.D,
+                                                 self.dtype)
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_kv_append_paged")
+
+    def decode(self, q, block_table, scale=None):
+        q, _ = _as_input(q)
+        bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+        B, Hq, D = q.shape
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        out = np.zeros((B, Hq, D), np.float64)
+        lse = np.zeros((B, Hq), np.float64)
+        rc = self.orc.lib.oracle_decode_paged(_ptr(q), _ptr(self.k), _ptr(self.v), self.dtype,
+                                              _ptr(bt), bt.shape[1], self.P, self.n_pages,
+                                              _ptr(self.len), B, Hq, self.Hkv, self.W, D,
+                                              float(scale), _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_decode_paged")
+        return out, lse
+
+
 _default = None
 
 
@@ -269,3 +321,7 @@ def fwd_rows(*a, **kw):
 
 def ring(*a, **kw) -> Ring:
     return default().ring(*a, **kw)
+
+
+def paged(*a, **kw) -> PagedCache:
+    return default().paged(*a, **kw)

@@ -469,6 +469,100 @@ int oracle_decode_sinks(const void* q, const void* kcache, const void* vcache,
     return 0;
 }
 
+/* ---- paged window cache ------------------------------------------------- */
+
+/* A shared pool of pages kpool, vpool [n_pages, Hkv, P, D]; a page holds P
+ * consecutive positions of one sequence for every kv head.  Sequence b keeps a
+ * circular block table of nb entries: position t lives in page
+ * block_table[b*nb + (t / P) % nb], slot t % P.  With nb*P >= W + P - 1 the
+ * blocks that intersect the last W positions have distinct table entries, so
+ * a table entry can be re-pointed (its old page released to the pool) once
+ * its block has left the window (mhpn.cn "Dilated sliding window", section 4,
+ * KV-cache management: out-of-window entries freed page by page;
+ * intelliparadigm.com, section 6: pre-allocated memory pool, cache updates
+ * without copies).  seq_len[b] counts the tokens appended so far. */
+
+/* Appends n tokens, k, v [B,n,Hkv,D], at positions seq_len[b] .. seq_len[b]+n-1.
+ * Only the last min(n, W) of them are written (older ones are out of every
+ * later window); the table entries of their blocks must already point to the
+ * pages the caller assigned.  Then seq_len[b] += n. */
+int oracle_kv_append_paged(void* kpool, void* vpool, const void* k, const void* v,
+                           const int32_t* block_table, int64_t nb, int64_t P, int64_t n_pages,
+                           int64_t* seq_len, int64_t B, int64_t Hkv, int64_t W, int64_t n,
+                           int64_t D, int dtype) {
+    if (B <= 0 || Hkv <= 0 || W <= 0 || P <= 0 || nb <= 0 || nb * P < W + P - 1 || n < 0 ||
+        D <= 0 || (dtype != 0 && dtype != 1))
+        return -1;
+    for (int64_t b = 0; b < B; b++) {
+        if (seq_len[b] < 0) return -1;
+        const int64_t first = n > W ? n - W : 0;
+        for (int64_t t = first; t < n; t++) {
+            const int64_t pos = seq_len[b] + t;
+            const int64_t page = block_table[b * nb + (pos / P) % nb];
+            if (page < 0 || page >= n_pages) return -1;
+            for (int64_t h = 0; h < Hkv; h++)
+                for (int64_t c = 0; c < D; c++) {
+                    int64_t di = ((page * Hkv + h) * P + pos % P) * D + c;
+                    int64_t si = ((b * n + t) * Hkv + h) * D + c;
+                    copy_elem(kpool, k, dtype, di, si);
+                    copy_elem(vpool, v, dtype, di, si);
+                }
+        }
+        seq_len[b] += n;
+    }
+    return 0;
+}
+
+/* One decode step: query (b, h) attends positions max(0, L - W) .. L - 1 of
+ * sequence b (L = seq_len[b], the newest token included), fetched through
+ * the block table.  out [B,Hq,D], lse [B,Hq] in double; L == 0 is an error. */
+int oracle_decode_paged(const void* q, const void* kpool, const void* vpool, int dtype,
+                        const int32_t* block_table, int64_t nb, int64_t P, int64_t n_pages,
+                        const int64_t* seq_len, int64_t B, int64_t Hq, int64_t Hkv, int64_t W,
+                        int64_t D, double scale, double* out, double* lse) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || W <= 0 || P <= 0 || nb <= 0 ||
+        nb * P < W + P - 1 || D <= 0 || (dtype != 0 && dtype != 1))
+        return -1;
+    for (int64_t b = 0; b < B; b++) {
+        if (seq_len[b] < 1) return -1;
+        for (int64_t pos = seq_len[b] > W ? seq_len[b] - W : 0; pos < seq_len[b]; pos++) {
+            const int64_t page = block_table[b * nb + (pos / P) % nb];
+            if (page < 0 || page >= n_pages) return -1;
+        }
+    }
+    const int64_t group = Hq / Hkv;
+    const size_t esz = dtype == 0 ? 4 : 2;
+#pragma omp parallel
+    {
+        void* kt = malloc(esz * (size_t)(W * D));
+        void* vt = malloc(esz * (size_t)(W * D));
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)W);
+        double* s = (double*)malloc(sizeof(double) * (size_t)W);
+        for (int64_t t = 0; t < W; t++) keys[t] = t;
+#pragma omp for schedule(static)
+        for (int64_t bh = 0; bh < B * Hq; bh++) {
+            const int64_t bb = bh / Hq, kvh = (bh % Hq) / group;
+            int64_t nk = 0;
+            for (int64_t pos = seq_len[bb] > W ? seq_len[bb] - W : 0; pos < seq_len[bb]; pos++) {
+                const int64_t page = block_table[bb * nb + (pos / P) % nb];
+                const int64_t base = ((page * Hkv + kvh) * P + pos % P) * D;
+                for (int64_t c = 0; c < D; c++) {
+                    copy_elem(kt, kpool, dtype, nk * D + c, base + c);
+                    copy_elem(vt, vpool, dtype, nk * D + c, base + c);
+                }
+                nk++;
+            }
+            attend_row(q, bh * D, kt, vt, 0, D, dtype, D, keys, nk, scale, s, out + bh * D,
+                       lse + bh);
+        }
+        free(kt);
+        free(vt);
+        free(keys);
+        free(s);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

@@ -443,9 +443,110 @@ def pin_decode_sinks(orc):
     _close(l1, l2, 0.0, "zero sinks lse")
 
 
+class _PagePool:
+    """Host bookkeeping of a paged window cache: a free list shared by all
+    sequences and, per sequence, the block held by each table entry.  Before
+    an append it points the entries of the blocks about to be written at
+    pages; a block that left the window gives its page back first."""
+
+    def __init__(self, n_pages, B, nb, P, W, order):
+        self.free = list(order)
+        self.table = np.full((B, nb), -1, np.int32)
+        self.block = np.full((B, nb), -1, np.int64)
+        self.nb, self.P, self.W = nb, P, W
+
+    def reserve(self, b, L, n):
+        first = L + max(0, n - self.W)
+        for blk in range(first // self.P, (L + n - 1) // self.P + 1):
+            j = blk % self.nb
+            if self.block[b, j] != blk:
+                if self.table[b, j] >= 0:
+                    self.free.append(int(self.table[b, j]))    # out of every window now
+                self.table[b, j] = self.free.pop(0)
+                self.block[b, j] = blk
+
+    def release(self, b):
+        for j in range(self.nb):
+            if self.table[b, j] >= 0:
+                self.free.append(int(self.table[b, j]))
+        self.table[b] = -1
+        self.block[b] = -1
+
+
+def pin_paged_stream(orc):
+    """Three sequences share a page pool smaller than their blocks; pages of
+    blocks that left the window go back to the pool and are reused, also by
+    other sequences.  Every decode step equals the dense-mask brute force of
+    the causal window-W forward of that sequence's tokens."""
+    B, Hq, Hkv, D, W, P, nb, n_pages = 3, 4, 2, 8, 10, 4, 4, 9
+    N = 40
+    q, k, v = fwd_inputs(330, B, Hq, Hkv, N, D, "bf16")
+    ref_o, _ = bruteforce.fwd(q, k, v, win_left=W - 1, win_right=0, scale=0.3)
+    rng = np.random.Generator(np.random.PCG64(331))
+    pool = _PagePool(n_pages, B, nb, P, W, rng.permutation(n_pages))
+    z = np.zeros((n_pages, Hkv, P, D), np.uint16)
+    cache = orc.paged(z, z, [0] * B, W)
+    # sequence 0 prefilled with a chunk longer than the window; 1 and 2 start empty
+    plan = {0: [23, 1, 1, 1], 1: [1] * 12, 2: [5, 1, 1]}
+    pos = [0] * B
+    for step in range(12):
+        for b in range(B):
+            if step >= len(plan[b]):
+                continue
+            n = plan[b][step]
+            pool.reserve(b, pos[b], n)
+            kb = np.zeros((B, n, Hkv, D), np.uint16)
+            vb = np.zeros_like(kb)
+            kb[b], vb[b] = k[b, pos[b]:pos[b] + n], v[b, pos[b]:pos[b] + n]
+            # one sequence per append call: the other rows append nothing
+            lens = cache.len.copy()
+            sub = orc.paged(cache.k, cache.v, [cache.len[b]], W)
+            sub.append(kb[b:b + 1], vb[b:b + 1], pool.table[b:b + 1])
+            cache.k, cache.v = sub.k, sub.v
+            cache.len = lens
+            cache.len[b] += n
+            pos[b] += n
+            qb = np.zeros((1, Hq, D), np.uint16)
+            qb[0] = q[b, pos[b] - 1]
+            sub = orc.paged(cache.k, cache.v, [cache.len[b]], W)
+            o, _ = sub.decode(qb, pool.table[b:b + 1], scale=0.3)
+            _close(o[0], ref_o[b, pos[b] - 1], 1e-12, f"paged seq {b} position {pos[b] - 1}")
+        if step == 4:
+            pool.release(2)                      # sequence 2 finished: all its pages return
+            assert len(set(pool.free)) == len(pool.free)
+    used = {int(x) for x in pool.table.reshape(-1) if x >= 0}
+    assert len(used) + len(pool.free) == n_pages and not used & set(pool.free)
+
+
+def pin_paged_equals_ring(orc):
+    """The same token stream through a W-slot ring and through the paged cache
+    gives the same decode rows; a batched paged append of several sequences at
+    once equals appending them one by one."""
+    B, Hq, Hkv, D, W, P, nb = 2, 2, 1, 8, 12, 8, 3
+    N = 30
+    q, k, v = fwd_inputs(332, B, Hq, Hkv, N, D, "f32")
+    ring = _empty_ring(orc, B, Hkv, W, D, "f32", [5, 0])
+    n_pages = B * nb
+    cache = orc.paged(np.zeros((n_pages, Hkv, P, D), np.float32),
+                      np.zeros((n_pages, Hkv, P, D), np.float32), [0] * B, W)
+    table = np.arange(B * nb, dtype=np.int32).reshape(B, nb)[:, ::-1].copy()  # in-place reuse
+    p0 = 0
+    for n in [17, 1, 1, 9, 1, 1]:
+        sl = slice(p0, p0 + n)
+        cache.append(np.ascontiguousarray(k[:, sl]), np.ascontiguousarray(v[:, sl]), table)
+        ring.append_chunk(np.ascontiguousarray(k[:, sl]), np.ascontiguousarray(v[:, sl]))
+        p0 += n
+        qt = np.ascontiguousarray(q[:, p0 - 1])
+        o1, l1 = cache.decode(qt, table, scale=0.2)
+        o2, l2 = ring.decode(qt, scale=0.2)
+        _close(o1, o2, 1e-12, f"paged vs ring at {p0}")
+        _close(l1, l2, 1e-12, f"paged vs ring lse at {p0}")
+
+
 ALL_PINS = [
     pin_dilated_index_sets, pin_dilated_span, pin_edge_truncation, pin_decode_demo_window,
     pin_ring_buffer_trace, pin_bruteforce, pin_bruteforce_mask_is_page_mask, pin_full_window,
     pin_zero_window, pin_q_zero, pin_dilation_strided, pin_gqa, pin_globals, pin_decode,
     pin_append_chunk, pin_chunked_prefill, pin_prefill_then_decode, pin_decode_sinks,
+    pin_paged_stream, pin_paged_equals_ring,
 ]

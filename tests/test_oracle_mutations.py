@@ -66,6 +66,13 @@ MUTATIONS = {
     "sinks_kv_head_modulo": ("kh = (bh % Hq) / group;", "kh = (bh % Hq) % Hkv;"),
     "sinks_ring_oldest_dropped": ("for (int64_t a = 0; a < cache_len[b]; a++) { /* the valid",
                                   "for (int64_t a = 0; a + 1 < cache_len[b]; a++) { /* the valid"),
+    "paged_write_slot": ("int64_t di = ((page * Hkv + h) * P + pos % P) * D + c;",
+                         "int64_t di = ((page * Hkv + h) * P + (pos + 1) % P) * D + c;"),
+    "paged_read_wrong_block": ("block_table[bb * nb + (pos / P) % nb];",
+                               "block_table[bb * nb + (pos / P + 1) % nb];"),
+    "paged_window_short": ("pos = seq_len[bb] > W ? seq_len[bb] - W : 0;",
+                           "pos = seq_len[bb] > W ? seq_len[bb] - W + 1 : 0;"),
+    "paged_count_not_advanced": ("        seq_len[b] += n;", "        seq_len[b] += n - (n > 1);"),
 }
 
 
