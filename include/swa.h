@@ -257,6 +257,63 @@ int swa_decode_sinks(const void* q, const void* kcache, const void* vcache,
 /* Bytes of device workspace swa_decode_sinks needs (0 on bad sizes). */
 size_t swa_decode_sinks_workspace_size(int B, int Hq, int W, int D, int n_sink);
 
+/*
+ * Paged window cache (mhpn.cn "Dilated sliding window", section 4, KV-cache
+ * management: entries that left the window are freed page by page;
+ * intelliparadigm.com, section 6: a pre-allocated memory pool, cache updates
+ * without copies).  Keys and values live in a pool of pages shared by all
+ * sequences:
+ *   kpool, vpool   device, [n_pages, Hkv, P, D] of `dtype`; a page holds P
+ *                  consecutive positions (P = page_size, a power of two) of
+ *                  one sequence for every kv head
+ *   block_table    device int32 [B, nb]: position t of sequence b is in page
+ *                  block_table[b*nb + (t / P) % nb], slot t % P.  nb*P must be
+ *                  at least W + P - 1, so that the blocks meeting the last W
+ *                  positions sit in distinct entries.
+ *   seq_len        device int32 [B]: tokens appended so far (positions
+ *                  0 .. seq_len[b] - 1)
+ * The caller owns the pool and the table and decides which page each entry
+ * points to.  Before an append it points the entries of the blocks the new
+ * positions fall in at pages; an entry whose block holds no position of the
+ * last W may be re-pointed, its page going back to the pool (eviction).
+ * Page ids out of [0, n_pages) are clamped into the pool (no fault; the
+ * result is then meaningless).
+ */
+
+/*
+ * swa_kv_append_paged: append n tokens per sequence, k, v [B, n, Hkv, D], at
+ * positions seq_len[b] .. seq_len[b] + n - 1; only the last min(n, W) are
+ * written (older ones are outside every later window).  Then seq_len[b] += n.
+ * n = 1 is the decode-step append; n > 1 hands a prefilled chunk over.
+ *
+ * Errors: SWA_ERR_ARG for null pointers (k, v may be NULL when n == 0),
+ * non-positive sizes, n < 0, n or W above SWA_MAX_N, page_size not a power of
+ * two up to 2^20, or nb*page_size < W + page_size - 1; SWA_ERR_UNSUPPORTED for
+ * D or dtype; SWA_ERR_HIP if a launch fails.
+ */
+int swa_kv_append_paged(void* kpool, void* vpool, const void* k, const void* v,
+                        const int32_t* block_table, int32_t* seq_len,
+                        int B, int Hkv, int n_pages, int page_size, int nb, int W, int n,
+                        int D, int dtype, hipStream_t stream);
+
+/*
+ * swa_decode_paged: one query token per sequence, q [B, Hq, D], attends the
+ * last min(seq_len[b], W) positions (the newest included) through the block
+ * table; the same result as swa_decode on a W-slot ring fed the same tokens.
+ *   out [B, Hq, D] of `dtype`; lse [B, Hq] float32 (may be NULL);
+ *   workspace of at least swa_decode_workspace_size(B, Hq, W, D) bytes.
+ * A sequence with seq_len == 0 gets out = 0, lse = -inf.
+ *
+ * Errors: as swa_kv_append_paged, plus SWA_ERR_ARG for Hq % Hkv != 0 and
+ * SWA_ERR_WORKSPACE when the workspace is NULL or too small.
+ */
+int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
+                     const int32_t* block_table, const int32_t* seq_len,
+                     void* out, float* lse,
+                     int B, int Hq, int Hkv, int n_pages, int page_size, int nb, int W, int D,
+                     float scale, void* workspace, size_t workspace_bytes, int dtype,
+                     hipStream_t stream);
+
 /* A static, human-readable description of a status code. */
 const char* swa_status_string(int status);
 

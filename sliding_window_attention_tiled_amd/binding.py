@@ -56,6 +56,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swa_decode_sinks.restype = I
     lib.swa_decode_sinks_workspace_size.argtypes = [I, I, I, I, I]
     lib.swa_decode_sinks_workspace_size.restype = SZ
+    lib.swa_kv_append_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P]
+    lib.swa_kv_append_paged.restype = I
+    lib.swa_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P, SZ, I,
+                                     P]
+    lib.swa_decode_paged.restype = I
     lib.swa_decode_workspace_size.argtypes = [I, I, I, I]
     lib.swa_decode_workspace_size.restype = SZ
     lib.swa_status_string.argtypes = [I]
@@ -288,4 +293,62 @@ def decode_sinks(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                               workspace.numel() * workspace.element_size(), _dtype_code(q),
                               _stream(q))
     _check(st, "swa_decode_sinks")
+    return (out, lse) if return_lse else out
+
+
+def _paged_state(kpool, vpool, block_table, seq_len, B):
+    if vpool.shape != kpool.shape or vpool.dtype != kpool.dtype:
+        raise SwaError(-1, "kpool and vpool must match")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise SwaError(-1, "block_table must be int32 [B, nb]")
+    if seq_len.dtype != torch.int32 or seq_len.shape != (B,):
+        raise SwaError(-1, "seq_len must be int32 [B]")
+
+
+def kv_append_paged(kpool: torch.Tensor, vpool: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    block_table: torch.Tensor, seq_len: torch.Tensor, *, window: int):
+    """Append k/v [B,n,Hkv,D] to a paged window cache (pool [n_pages,Hkv,P,D])."""
+    lib = load_library()
+    n_pages, Hkv, P, D = kpool.shape
+    B, n = k.shape[0], k.shape[1]
+    if k.shape != (B, n, Hkv, D) or v.shape != k.shape or k.dtype != kpool.dtype:
+        raise SwaError(-1, "kv_append_paged shape or dtype mismatch")
+    _paged_state(kpool, vpool, block_table, seq_len, B)
+    st = lib.swa_kv_append_paged(_dev(kpool, "kpool"), _dev(vpool, "vpool"),
+                                 _dev(k, "k") if n else None, _dev(v, "v") if n else None,
+                                 _dev(block_table, "block_table"), _dev(seq_len, "seq_len"),
+                                 B, Hkv, n_pages, P, block_table.shape[1], window, n, D,
+                                 _dtype_code(kpool), _stream(kpool))
+    _check(st, "swa_kv_append_paged")
+
+
+def decode_paged(q: torch.Tensor, kpool: torch.Tensor, vpool: torch.Tensor,
+                 block_table: torch.Tensor, seq_len: torch.Tensor, *, window: int,
+                 scale: float | None = None, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                 return_lse: bool = True):
+    """One decode step over the last `window` positions of a paged cache."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    n_pages, Hkv, P, _ = kpool.shape
+    if kpool.shape[3] != D or kpool.dtype != q.dtype:
+        raise SwaError(-1, "decode_paged shape or dtype mismatch")
+    _paged_state(kpool, vpool, block_table, seq_len, B)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_size(B, Hq, window, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.swa_decode_paged(_dev(q, "q"), _dev(kpool, "kpool"), _dev(vpool, "vpool"),
+                              _dev(block_table, "block_table"), _dev(seq_len, "seq_len"),
+                              _dev(out, "out"), _dev(lse, "lse"), B, Hq, Hkv, n_pages, P,
+                              block_table.shape[1], window, D, float(scale),
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _dtype_code(q),
+                              _stream(q))
+    _check(st, "swa_decode_paged")
     return (out, lse) if return_lse else out

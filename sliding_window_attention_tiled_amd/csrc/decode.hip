@@ -78,6 +78,48 @@ __global__ __launch_bounds__(64) void ring_advance_kernel(int32_t* head, int32_t
     len[b] = (int32_t)min<int64_t>((int64_t)max(len[b], 0) + n, W);
 }
 
+// ---- paged cache append ----------------------------------------------------------
+// Positions seq_len[b] + t (t = n - m .. n - 1, m = min(n, W)) of sequence b go
+// to their page block_table[b][(pos / P) % nb], slot pos % P.  Page ids are
+// device data: they are clamped into the pool so that no write leaves it.
+__global__ __launch_bounds__(256) void kv_append_paged_kernel(
+    unsigned char* kpool, unsigned char* vpool, const unsigned char* k, const unsigned char* v,
+    const int32_t* table, const int32_t* seq_len, int Hkv, int n_pages, int page_shift, int nb,
+    int n, int m, int row_bytes, int bps) {
+    const int b = blockIdx.x / bps;
+    const int cpr = row_bytes / 16;
+    const int64_t total = (int64_t)m * Hkv * cpr;
+    const int64_t ci = (int64_t)(blockIdx.x % bps) * blockDim.x + threadIdx.x;
+    if (ci >= total) return;
+    const int c = (int)(ci % cpr);
+    const int h = (int)((ci / cpr) % Hkv);
+    const int64_t t = n - m + ci / ((int64_t)cpr * Hkv);
+    const int64_t pos = (int64_t)max(seq_len[b], 0) + t;
+    int page = table[(size_t)b * nb + (int)((pos >> page_shift) % nb)];
+    page = min(max(page, 0), n_pages - 1);
+    const int64_t slot = pos & ((1 << page_shift) - 1);
+    const size_t src = (((size_t)b * n + t) * Hkv + h) * row_bytes + c * 16;
+    const size_t dst = ((((size_t)page * Hkv + h) << page_shift) + slot) * row_bytes + c * 16;
+    *(u32x4*)(kpool + dst) = *(const u32x4*)(k + src);
+    *(u32x4*)(vpool + dst) = *(const u32x4*)(v + src);
+}
+
+__global__ __launch_bounds__(64) void seq_advance_kernel(int32_t* seq_len, int B, int n) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) seq_len[b] = max(seq_len[b], 0) + n;
+}
+
+// Element offset of the row of window index i (0 = oldest live position) in
+// the page pool, for (b, kv head) of a paged decode.
+__device__ __forceinline__ size_t paged_row(const DecodeParams& p, int b, int kvh, int pos0,
+                                            int i, int D) {
+    const int pos = pos0 + i;
+    int page = p.block_table[(size_t)b * p.nb + ((pos >> p.page_shift) % p.nb)];
+    page = min(max(page, 0), p.n_pages - 1);
+    return ((((size_t)page * p.Hkv + kvh) << p.page_shift) + (pos & ((1 << p.page_shift) - 1))) *
+           D;
+}
+
 // ---- bf16 split decode on MFMA ----------------------------------------------------
 constexpr int CH = 32;        // slots per chunk
 constexpr int DNT = 256;      // 4 waves
@@ -90,7 +132,9 @@ struct DecCfg {
     static constexpr int WAVE_ELEMS = 2 * CH * PITCH; // K and V of one chunk
 };
 
-template <int D>
+// PAGED: the W slots are the window positions seq_len - min(seq_len, W) + i,
+// read through the block table; otherwise the ring's physical slots.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams p) {
     using C = DecCfg<D>;
     constexpr int KS = D / 32;   // 32-deep k-steps of S^T = K Q^T (16x16x32)
@@ -117,10 +161,14 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     const int hq = kvh * p.group + head_col;
 
     // the last split (when there are sinks) walks the sink entries, all valid
-    const bool sink_split = s >= p.ring_splits;
+    const bool sink_split = !PAGED && s >= p.ring_splits;
     const int W = p.W;
-    const int ring_head = p.ring_head[b];
-    const int cache_len = p.cache_len[b];
+    const int ring_head = PAGED ? 0 : p.ring_head[b];
+    // paged: live window positions pos0 .. pos0 + n_live - 1
+    const int seq_n = PAGED ? max(p.seq_len[b], 0) : 0;
+    const int n_live = min(seq_n, W);
+    const int pos0 = seq_n - n_live;
+    const int cache_len = PAGED ? n_live : p.cache_len[b];
     const bool full = sink_split || cache_len >= W;
     const int src_slots = sink_split ? p.n_sink : W;
 
@@ -141,7 +189,7 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             qreg[k] = head_ok ? *(const bf16x8*)(qp + k * 32)
                               : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    const size_t slab = ((size_t)b * p.Hkv + kvh) * src_slots;
+    const size_t slab = PAGED ? 0 : ((size_t)b * p.Hkv + kvh) * src_slots;
     const __bf16* kbase = (const __bf16*)(sink_split ? p.ksink : p.kcache) + slab * D;
     const __bf16* vbase = (const __bf16*)(sink_split ? p.vsink : p.vcache) + slab * D;
     unsigned short* Ks = smem + wave * C::WAVE_ELEMS;
@@ -160,8 +208,9 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
         for (int u = 0; u < C::PER_LANE; u++) {
             const int ci = lane + u * 64;
             const int key = ci / C::CPR, cc = ci % C::CPR;
-            if (base + key < w_hi) {
-                const size_t off = (size_t)(base + key) * D + cc * 8;
+            if (base + key < w_hi && (!PAGED || base + key < n_live)) {
+                const size_t off = (PAGED ? paged_row(p, b, kvh, pos0, base + key, D)
+                                          : (size_t)(base + key) * D) + cc * 8;
                 kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
                 vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
             } else {
@@ -201,7 +250,9 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             for (int e = 0; e < 4; e++) {
                 const int slot = base + kb * 16 + grp * 4 + e;
                 bool valid = slot < w_hi;
-                if (!full) {
+                if (PAGED) {
+                    valid = valid && slot < n_live;
+                } else if (!full) {
                     int age = ring_head - 1 - slot;
                     if (age < 0) age += W;
                     valid = valid && age < cache_len;
@@ -288,7 +339,7 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
 // ---- float32 split decode on the vector ALUs -------------------------------------
 // One wave per (b, query head, split); lanes 16*r .. 16*r+15 share a slot, each
 // lane a D/16 slice of it; four slots per step.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
     constexpr int DL = D / 16;
     const int lane = threadIdx.x;
@@ -299,10 +350,13 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
     const int hq = L % p.Hq;
     const int b = L / p.Hq;
     const int kvh = hq / p.group;
-    const bool sink_split = s >= p.ring_splits;  // sink entries: all valid
+    const bool sink_split = !PAGED && s >= p.ring_splits;  // sink entries: all valid
     const int W = p.W;
-    const int ring_head = p.ring_head[b];
-    const int cache_len = sink_split ? W : p.cache_len[b];
+    const int ring_head = PAGED ? 0 : p.ring_head[b];
+    const int seq_n = PAGED ? max(p.seq_len[b], 0) : 0;
+    const int n_live = min(seq_n, W);
+    const int pos0 = seq_n - n_live;
+    const int cache_len = sink_split ? W : PAGED ? n_live : p.cache_len[b];
     const int src_slots = sink_split ? p.n_sink : W;
     const int s_lo = sink_split ? 0 : s * p.slots_per_split;
     const int s_hi = sink_split ? p.n_sink : min(W, s_lo + p.slots_per_split);
@@ -311,7 +365,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
     const float* qp = (const float*)p.q + ((size_t)b * p.Hq + hq) * D + part * DL;
 #pragma unroll
     for (int d = 0; d < DL; d++) q[d] = qp[d];
-    const size_t slab = ((size_t)b * p.Hkv + kvh) * src_slots;
+    const size_t slab = PAGED ? 0 : ((size_t)b * p.Hkv + kvh) * src_slots;
     const float* kbase = (const float*)(sink_split ? p.ksink : p.kcache) + slab * D + part * DL;
     const float* vbase = (const float*)(sink_split ? p.vsink : p.vcache) + slab * D + part * DL;
     float acc[DL];
@@ -322,15 +376,19 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
     for (int base = s_lo; base < s_hi; base += 4) {
         const int slot = base + sub;
         bool valid = slot < s_hi;
-        if (valid && cache_len < W) {
+        if (PAGED) {
+            valid = valid && slot < n_live;
+        } else if (valid && cache_len < W) {
             int age = ring_head - 1 - slot;
             if (age < 0) age += W;
             valid = age < cache_len;
         }
+        const size_t row = PAGED ? (valid ? paged_row(p, b, kvh, pos0, slot, D) : 0)
+                                 : (size_t)slot * D;
         float dot = 0.f;
-        if (slot < s_hi) {
+        if (PAGED ? valid : slot < s_hi) {
 #pragma unroll
-            for (int d = 0; d < DL; d++) dot = __builtin_fmaf(q[d], kbase[(size_t)slot * D + d], dot);
+            for (int d = 0; d < DL; d++) dot = __builtin_fmaf(q[d], kbase[row + d], dot);
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) dot += __shfl_xor(dot, o);
@@ -348,7 +406,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
         l_run += pk;
         if (valid) {
 #pragma unroll
-            for (int d = 0; d < DL; d++) acc[d] = __builtin_fmaf(pk, vbase[(size_t)slot * D + d], acc[d]);
+            for (int d = 0; d < DL; d++) acc[d] = __builtin_fmaf(pk, vbase[row + d], acc[d]);
         }
     }
     // merge the four slot lanes (sub = 0..3) of each dim slice
@@ -449,21 +507,51 @@ hipError_t launch_kv_append_chunk(void* kc, void* vc, const void* k, const void*
     return hipGetLastError();
 }
 
-hipError_t launch_decode_bf16(const DecodeParams& p, int D, hipStream_t s) {
-    const int grid = p.B * p.Hkv * ((p.group + 15) / 16) * p.splits;
-    if (D == 128)
-        hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3(grid), dim3(DNT), 0, s, p);
-    else
-        hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(grid), dim3(DNT), 0, s, p);
+hipError_t launch_kv_append_paged(void* kpool, void* vpool, const void* k, const void* v,
+                                  const int32_t* block_table, int32_t* seq_len, int B, int Hkv,
+                                  int n_pages, int page_shift, int nb, int W, int n, int D,
+                                  int elem_bytes, hipStream_t s) {
+    const int m = n < W ? n : W;
+    const int row_bytes = D * elem_bytes;
+    const int64_t bps = ((int64_t)m * Hkv * (row_bytes / 16) + 255) / 256;
+    if (bps * B > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kv_append_paged_kernel, dim3((unsigned)(bps * B)), dim3(256), 0, s,
+                       (unsigned char*)kpool, (unsigned char*)vpool, (const unsigned char*)k,
+                       (const unsigned char*)v, block_table, (const int32_t*)seq_len, Hkv,
+                       n_pages, page_shift, nb, n, m, row_bytes, (int)bps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seq_advance_kernel, dim3((B + 63) / 64), dim3(64), 0, s, seq_len, B, n);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_f32(const DecodeParams& p, int D, hipStream_t s) {
+template <bool PAGED>
+void launch_decode_bf16_t(const DecodeParams& p, int D, hipStream_t s) {
+    const int grid = p.B * p.Hkv * ((p.group + 15) / 16) * p.splits;
+    if (D == 128)
+        hipLaunchKernelGGL((decode_bf16_kernel<128, PAGED>), dim3(grid), dim3(DNT), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_bf16_kernel<64, PAGED>), dim3(grid), dim3(DNT), 0, s, p);
+}
+
+template <bool PAGED>
+void launch_decode_f32_t(const DecodeParams& p, int D, hipStream_t s) {
     const int grid = p.B * p.Hq * p.splits;
     if (D == 128)
-        hipLaunchKernelGGL(decode_f32_kernel<128>, dim3(grid), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((decode_f32_kernel<128, PAGED>), dim3(grid), dim3(64), 0, s, p);
     else
-        hipLaunchKernelGGL(decode_f32_kernel<64>, dim3(grid), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((decode_f32_kernel<64, PAGED>), dim3(grid), dim3(64), 0, s, p);
+}
+
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, bool paged, hipStream_t s) {
+    if (paged) launch_decode_bf16_t<true>(p, D, s);
+    else launch_decode_bf16_t<false>(p, D, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_f32(const DecodeParams& p, int D, bool paged, hipStream_t s) {
+    if (paged) launch_decode_f32_t<true>(p, D, s);
+    else launch_decode_f32_t<false>(p, D, s);
     return hipGetLastError();
 }
 

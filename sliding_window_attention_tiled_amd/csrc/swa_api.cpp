@@ -64,6 +64,29 @@ bool plan_band(FwdParams& p, int dtype, swa::FwdShape* shape_out) {
     return true;
 }
 
+// Merges the split partials of a decode launch into out / lse.
+int combine_decode(const DecodeParams& p, void* out, float* lse, int D, int dtype,
+                   hipStream_t stream) {
+    CombineParams c;
+    std::memset(&c, 0, sizeof c);
+    c.partials = p.partials;
+    c.out = out;
+    c.lse = lse;
+    c.rows = p.B * p.Hq;
+    c.splits = p.splits;
+    c.mode = 0;
+    c.B = p.B;
+    c.Hq = p.Hq;
+    return swa::launch_combine(c, D, dtype, stream) == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+}
+
+// log2 of a power of two in [1, 2^20], else -1
+int page_shift_of(int P) {
+    for (int sh = 0; sh <= 20; sh++)
+        if (P == (1 << sh)) return sh;
+    return -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -270,21 +293,10 @@ int swa_decode_sinks(const void* q, const void* kcache, const void* vcache,
     p.vsink = vsink;
     p.n_sink = n_sink;
     p.splits = p.ring_splits + (n_sink > 0 ? 1 : 0);
-    hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, stream)
-                                     : swa::launch_decode_f32(p, D, stream);
+    hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, false, stream)
+                                     : swa::launch_decode_f32(p, D, false, stream);
     if (e != hipSuccess) return SWA_ERR_HIP;
-    CombineParams c;
-    std::memset(&c, 0, sizeof c);
-    c.partials = p.partials;
-    c.out = out;
-    c.lse = lse;
-    c.rows = B * Hq;
-    c.splits = p.splits;
-    c.mode = 0;
-    c.B = B;
-    c.Hq = Hq;
-    if (swa::launch_combine(c, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
-    return SWA_OK;
+    return combine_decode(p, out, lse, D, dtype, stream);
 }
 
 int swa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ring_head,
@@ -294,6 +306,64 @@ int swa_decode(const void* q, const void* kcache, const void* vcache, const int3
     return swa_decode_sinks(q, kcache, vcache, ring_head, cache_len, nullptr, nullptr, 0, out,
                             lse, B, Hq, Hkv, W, D, scale, workspace, workspace_bytes, dtype,
                             stream);
+}
+
+int swa_kv_append_paged(void* kpool, void* vpool, const void* k, const void* v,
+                        const int32_t* block_table, int32_t* seq_len, int B, int Hkv,
+                        int n_pages, int page_size, int nb, int W, int n, int D, int dtype,
+                        hipStream_t stream) {
+    if (!kpool || !vpool || !block_table || !seq_len) return SWA_ERR_ARG;
+    if (n > 0 && (!k || !v)) return SWA_ERR_ARG;
+    if (B <= 0 || Hkv <= 0 || n_pages <= 0 || nb <= 0 || W <= 0 || W > kMaxN || n < 0 ||
+        n > kMaxN || D <= 0)
+        return SWA_ERR_ARG;
+    const int sh = page_shift_of(page_size);
+    if (sh < 0 || (int64_t)nb * page_size < (int64_t)W + page_size - 1) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    if (n == 0) return SWA_OK;
+    const int elem = dtype == SWA_BF16 ? 2 : 4;
+    hipError_t e = swa::launch_kv_append_paged(kpool, vpool, k, v, block_table, seq_len, B, Hkv,
+                                               n_pages, sh, nb, W, n, D, elem, stream);
+    return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+}
+
+int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
+                     const int32_t* block_table, const int32_t* seq_len, void* out, float* lse,
+                     int B, int Hq, int Hkv, int n_pages, int page_size, int nb, int W, int D,
+                     float scale, void* workspace, size_t workspace_bytes, int dtype,
+                     hipStream_t stream) {
+    if (!q || !kpool || !vpool || !block_table || !seq_len || !out) return SWA_ERR_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || n_pages <= 0 || nb <= 0 || W <= 0 ||
+        W > kMaxN || D <= 0)
+        return SWA_ERR_ARG;
+    const int sh = page_shift_of(page_size);
+    if (sh < 0 || (int64_t)nb * page_size < (int64_t)W + page_size - 1) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < swa_decode_workspace_size(B, Hq, W, D))
+        return SWA_ERR_WORKSPACE;
+    DecodeParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.kcache = kpool;
+    p.vcache = vpool;
+    p.partials = (float*)workspace;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.W = W;
+    p.group = Hq / Hkv;
+    p.scale_log2 = scale * kLog2e;
+    decode_splits(B, Hq, W, &p.ring_splits, &p.slots_per_split);
+    p.splits = p.ring_splits;
+    p.block_table = block_table;
+    p.seq_len = seq_len;
+    p.n_pages = n_pages;
+    p.page_shift = sh;
+    p.nb = nb;
+    hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, true, stream)
+                                     : swa::launch_decode_f32(p, D, true, stream);
+    if (e != hipSuccess) return SWA_ERR_HIP;
+    return combine_decode(p, out, lse, D, dtype, stream);
 }
 
 }  // extern "C"

@@ -75,6 +75,12 @@ struct DecodeParams {
     const void* ksink;
     const void* vsink;
     int n_sink;
+    // paged cache (paged kernels only): kcache/vcache are the page pool
+    // [n_pages][Hkv][P][D], P = 1 << page_shift; position t of sequence b is in
+    // page block_table[b * nb + (t >> page_shift) % nb]; seq_len[b] tokens so far
+    const int32_t* block_table;
+    const int32_t* seq_len;
+    int n_pages, page_shift, nb;
 };
 
 struct CombineParams {
@@ -107,8 +113,12 @@ hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn,
 hipError_t launch_kv_append_chunk(void* kc, void* vc, const void* k, const void* v,
                                   int32_t* head, int32_t* len, int B, int Hkv, int W, int n,
                                   int D, int elem_bytes, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeParams& p, int D, hipStream_t s);
-hipError_t launch_decode_f32(const DecodeParams& p, int D, hipStream_t s);
+hipError_t launch_kv_append_paged(void* kpool, void* vpool, const void* k, const void* v,
+                                  const int32_t* block_table, int32_t* seq_len, int B, int Hkv,
+                                  int n_pages, int page_shift, int nb, int W, int n, int D,
+                                  int elem_bytes, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, bool paged, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams& p, int D, bool paged, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t s);
 
 }  // namespace swa

@@ -33,7 +33,7 @@ def test_header_declares_entry_points():
     for n in ["swa_fwd", "swa_fwd_workspace_size", "swa_kv_append", "swa_decode",
               "swa_decode_workspace_size", "swa_status_string", "swa_version",
               "swa_kv_append_chunk", "swa_fwd_cached", "swa_decode_sinks",
-              "swa_decode_sinks_workspace_size"]:
+              "swa_decode_sinks_workspace_size", "swa_kv_append_paged", "swa_decode_paged"]:
         assert n in names
 
 
@@ -202,3 +202,40 @@ def test_decode_sinks_validation(lib):
     assert call(D=80) == UNSUP
     assert call(wsb=need - 4) == WS
     assert call(ws=None) == WS
+
+
+def test_paged_validation(lib):
+    fa = lib.swa_kv_append_paged
+    # (kpool, vpool, k, v, table, seq, B, Hkv, n_pages, P, nb, W, n, D, dtype, stream)
+    ok = [P, P, P, P, P, P, 2, 2, 16, 16, 8, 100, 3, 128, 1, None]
+
+    def app(**ch):
+        names = ["kp", "vp", "k", "v", "bt", "sl", "B", "Hkv", "np", "P", "nb", "W", "n", "D",
+                 "dt", "st"]
+        a = list(ok)
+        for k_, v_ in ch.items():
+            a[names.index(k_)] = v_
+        return fa(*a)
+    assert app(kp=None) == ARG and app(bt=None) == ARG and app(sl=None) == ARG
+    assert app(k=None) == ARG
+    assert app(k=None, v=None, n=0) == OK
+    assert app(P=24) == ARG                       # not a power of two
+    assert app(nb=7) == ARG                       # 7 * 16 < 100 + 15
+    assert app(nb=8, W=114) == ARG                # 8 * 16 < 114 + 15
+    assert app(n=-1) == ARG and app(np=0) == ARG
+    assert app(D=96) == UNSUP and app(dt=4) == UNSUP
+    fd = lib.swa_decode_paged
+    need = lib.swa_decode_workspace_size(2, 8, 100, 128)
+    okd = [P, P, P, P, P, P, None, 2, 8, 2, 16, 16, 8, 100, 128, 0.1, P, need, 1, None]
+
+    def dec(**ch):
+        names = ["q", "kp", "vp", "bt", "sl", "out", "lse", "B", "Hq", "Hkv", "np", "P", "nb",
+                 "W", "D", "scale", "ws", "wsb", "dt", "st"]
+        a = list(okd)
+        for k_, v_ in ch.items():
+            a[names.index(k_)] = v_
+        return fd(*a)
+    assert dec(q=None) == ARG and dec(bt=None) == ARG and dec(out=None) == ARG
+    assert dec(Hq=6, Hkv=4) == ARG and dec(P=12) == ARG and dec(nb=7) == ARG
+    assert dec(D=80) == UNSUP
+    assert dec(ws=None) == WS and dec(wsb=need - 1) == WS
