@@ -11,7 +11,8 @@ K+V streamed, and the fp64 CPU oracle timed on a bounded sample of rows.
 
 Also reported, per call: the bidirectional encoder with global tokens, the
 four layers of the dilated stack and one 4096-token chunk of a chunked prefill
-(exact TFLOP/s against min(MFMA peak, HBM peak x arithmetic intensity)).
+(exact TFLOP/s against min(MFMA peak, HBM peak x arithmetic intensity)), and
+the decode shape with four attention sinks and through a paged pool (GB/s).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
                     [--no-others]
@@ -309,6 +310,61 @@ def bench_other_workloads():
     res.append(_report("prefill_chunk4096_after_full_ring", ms, mn, flop, bytes_,
                        {"append_chunk_ms": round(ams, 4),
                         "append_chunk_gbs": round(append_bytes / (ams * 1e-3) / 1e9, 1)}))
+    del q, k, v, kc, vc, kc2, vc2, out, lse
+    res.extend(bench_decode_variants())
+    return res
+
+
+def _decode_report(name, ms, ms_min, kv_bytes, extra=None):
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    r = {"workload": name, "kernel_ms": round(ms, 4), "kernel_ms_min": round(ms_min, 4),
+         "kv_bytes": int(kv_bytes), "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    if extra:
+        r.update(extra)
+    return r
+
+
+def bench_decode_variants():
+    """The rolling-cache decode shape (64 sequences, Hq=32, Hkv=8, D=128, window
+    4096) with four attention-sink entries, and through a paged pool of
+    64-position pages placed at random: one decode call timed per step, K+V
+    bytes of the attended entries per call."""
+    import torch
+    from sliding_window_attention_tiled_amd import binding, configs
+    from sliding_window_attention_tiled_amd.inputs import DecodeInputs
+
+    c = configs.DECODE
+    B, Hq, Hkv, W, D = c["B"], c["Hq"], c["Hkv"], c["W"], c["D"]
+    res = []
+    gen = DecodeInputs(c["seed"], B, Hq, Hkv, W, D, c["dtype"])
+    kc, vc = to_dev(gen.kcache), to_dev(gen.vcache)
+    head = torch.from_numpy(gen.ring_head.copy()).to("cuda")
+    length = torch.from_numpy(gen.cache_len.copy()).to("cuda")
+    qd = to_dev(gen.step()[0])
+    S = 4
+    sk = DecodeInputs(c["seed"] + 10, B, Hq, Hkv, S, D, c["dtype"])
+    ks, vs = to_dev(sk.kcache), to_dev(sk.vcache)
+    ws = torch.empty(binding.decode_sinks_workspace_size(B, Hq, W, D, S), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ms, mn = _time_calls(lambda: binding.decode_sinks(qd, kc, vc, head, length, ks, vs,
+                                                      workspace=ws, out=out, lse=lse))
+    res.append(_decode_report("decode_ring4096_sinks4", ms, mn,
+                              2.0 * B * Hkv * (W + S) * D * 2))
+    del kc, vc
+    P = 64
+    nb = (W + P - 1 + P - 1) // P
+    n_pages = B * nb
+    pg = DecodeInputs(c["seed"] + 20, n_pages, Hq, Hkv, P, D, c["dtype"])
+    kp, vp = to_dev(pg.kcache), to_dev(pg.vcache)
+    g = np.random.Generator(np.random.PCG64(c["seed"] + 21))
+    table = torch.from_numpy(g.permutation(n_pages).astype(np.int32).reshape(B, nb)).to("cuda")
+    seq = torch.from_numpy(g.integers(W, 3 * W, size=B).astype(np.int32)).to("cuda")
+    ms, mn = _time_calls(lambda: binding.decode_paged(qd, kp, vp, table, seq, window=W,
+                                                      workspace=ws, out=out, lse=lse))
+    res.append(_decode_report("decode_paged_p64_window4096", ms, mn,
+                              2.0 * B * Hkv * W * D * 2, {"page_size": P}))
     return res
 
 

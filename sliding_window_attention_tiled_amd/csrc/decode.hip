@@ -201,6 +201,33 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     float m_run = kEmptyMax, l_run = 0.f;
     const float c = p.scale_log2;
 
+    // paged: the wave's pages are looked up once, one per lane (block fb + lane),
+    // and each key finds its page with a lane permute, so a chunk's loads do not
+    // wait on a table read.  Wave ranges spanning more than 64 pages (pages
+    // shorter than a 64th of the range) read the table per key instead.
+    int fb = 0, my_page = 0;
+    bool lane_pages = false;
+    if (PAGED && w_lo < w_hi) {
+        fb = (pos0 + w_lo) >> p.page_shift;
+        const int nblk = ((pos0 + w_hi - 1) >> p.page_shift) - fb + 1;
+        lane_pages = nblk <= 64;
+        if (lane_pages && lane < nblk) {
+            const int pg = p.block_table[(size_t)b * p.nb + ((fb + lane) % p.nb)];
+            my_page = min(max(pg, 0), p.n_pages - 1);
+        }
+    }
+    // page of window index i from the lane copies; every lane takes part in the
+    // permute (lanes whose key is out of range discard the result)
+    auto lane_page = [&](int i) -> int {
+        return __builtin_amdgcn_ds_bpermute((((pos0 + i) >> p.page_shift) - fb) << 2, my_page);
+    };
+    auto page_row = [&](int i, int pg) -> size_t {
+        const int pos = pos0 + i;
+        if (!lane_pages) return paged_row(p, b, kvh, pos0, i, D);
+        return ((((size_t)pg * p.Hkv + kvh) << p.page_shift) +
+                (pos & ((1 << p.page_shift) - 1))) * D;
+    };
+
     u32x4 kr[C::PER_LANE], vr[C::PER_LANE];
     auto load_chunk = [&](int ck) {
         const int base = w_lo + ck * CH;
@@ -208,8 +235,9 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
         for (int u = 0; u < C::PER_LANE; u++) {
             const int ci = lane + u * 64;
             const int key = ci / C::CPR, cc = ci % C::CPR;
+            const int pg = PAGED && lane_pages ? lane_page(base + key) : 0;
             if (base + key < w_hi && (!PAGED || base + key < n_live)) {
-                const size_t off = (PAGED ? paged_row(p, b, kvh, pos0, base + key, D)
+                const size_t off = (PAGED ? page_row(base + key, pg)
                                           : (size_t)(base + key) * D) + cc * 8;
                 kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
                 vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
