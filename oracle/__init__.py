@@ -94,6 +94,9 @@ class OracleLib:
         lib.oracle_decode_paged.argtypes = [P, P, P, I, P, I64, I64, I64, P, I64, I64, I64, I64,
                                             I64, D, P, P]
         lib.oracle_decode_paged.restype = I
+        lib.oracle_bwd.argtypes = [P, P, P, P, I, I64, I64, I64, I64, I64, I64, I64, I64, P,
+                                   I64, D, P, P, P]
+        lib.oracle_bwd.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         self.lib = lib
@@ -157,6 +160,31 @@ class OracleLib:
         if rc != 0:
             raise ValueError("invalid arguments to oracle_fwd_rows")
         return out, lse
+
+    def bwd(self, q, k, v, dout, *, win_left: int, win_right: int = 0, dilation: int = 1,
+            global_idx=None, scale=None):
+        """Gradients (dq [B,N,Hq,D], dk, dv [B,N,Hkv,D]) in float64 for the upstream
+        gradient dout [B,N,Hq,D] of the forward with the same arguments."""
+        q, dt = _as_input(q)
+        k, _ = _as_input(k)
+        v, _ = _as_input(v)
+        dout, dt2 = _as_input(dout)
+        if dt2 != dt:
+            raise TypeError("dout must have the element type of q")
+        B, N, Hq, D = q.shape
+        Hkv = k.shape[2]
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        g, ng = _globals(global_idx)
+        dq = np.zeros((B, N, Hq, D), np.float64)
+        dk = np.zeros((B, N, Hkv, D), np.float64)
+        dv = np.zeros((B, N, Hkv, D), np.float64)
+        rc = self.lib.oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, B, Hq, Hkv, N, D,
+                                 win_left, win_right, dilation, _ptr(g), ng, float(scale),
+                                 _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_bwd")
+        return dq, dk, dv
 
     def ring(self, kcache, vcache, ring_head, cache_len) -> "Ring":
         return Ring(self, kcache, vcache, ring_head, cache_len)
@@ -317,6 +345,10 @@ def fwd(*a, **kw):
 
 def fwd_rows(*a, **kw):
     return default().fwd_rows(*a, **kw)
+
+
+def bwd(*a, **kw):
+    return default().bwd(*a, **kw)
 
 
 def ring(*a, **kw) -> Ring:

@@ -237,6 +237,82 @@ int oracle_fwd(const void* q, const void* k, const void* v, int dtype,
     return rc;
 }
 
+/* ---- backward ---------------------------------------------------------- */
+
+/* Gradients of the forward above for an upstream gradient dout [B,N,Hq,D]
+ * (the training use of the window attention: bmjup.com Q&A "training vs
+ * inference"; intelliparadigm.com section 5.1, blocked computation and
+ * mixed-precision training with a backward pass).  With
+ * P_ij = exp(s_ij - M_i) / L_i over j in S(i) and dP_ij = dout_i . v_j:
+ *   dv_j += P_ij dout_i
+ *   dS_ij = P_ij (dP_ij - sum_{j' in S(i)} P_ij' dP_ij')
+ *   dq_i  = scale sum_j dS_ij k_j,   dk_j += scale dS_ij q_i
+ * (the chain rule through s = scale q.k, softmax and the weighted sum; a kv
+ * head collects the terms of every query head that reads it).  dq [B,N,Hq,D],
+ * dk, dv [B,N,Hkv,D] in double. */
+int oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+               int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+               int64_t wl, int64_t wr, int64_t dil, const int32_t* gidx, int64_t ng,
+               double scale, double* dq, double* dk, double* dv) {
+    if (!fwd_args_ok(B, Hq, Hkv, N, D, wl, wr, dil, dtype)) return -1;
+    for (int64_t t = 0; t < ng; t++)
+        if (gidx[t] < 0 || gidx[t] >= N) return -1;
+    int64_t* G = (int64_t*)malloc(sizeof(int64_t) * (size_t)(ng > 0 ? ng : 1));
+    int64_t nG = normalise_globals(gidx, ng, G);
+    const int64_t group = Hq / Hkv;
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + wl + wr + nG + 1));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(N + wl + wr + nG + 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(N + wl + wr + nG + 1));
+    for (int64_t x = 0; x < B * N * Hkv * D; x++) dk[x] = dv[x] = 0.0;
+    /* serial over rows: dk and dv are sums over many rows */
+    for (int64_t b = 0; b < B; b++)
+        for (int64_t h = 0; h < Hq; h++)
+            for (int64_t i = 0; i < N; i++) {
+                const int64_t kh = h / group;
+                const int64_t nk = attended_set(i, N, wl, wr, dil, G, nG, keys);
+                const int64_t qo = ((b * N + i) * Hq + h) * D;
+                double M = -INFINITY;
+                for (int64_t t = 0; t < nk; t++) {
+                    const int64_t ko = ((b * N + keys[t]) * Hkv + kh) * D;
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < D; c++)
+                        dot += load_elem(q, dtype, qo + c) * load_elem(k, dtype, ko + c);
+                    p[t] = scale * dot;
+                    if (p[t] > M) M = p[t];
+                }
+                double L = 0.0;
+                for (int64_t t = 0; t < nk; t++) {
+                    p[t] = exp(p[t] - M);
+                    L += p[t];
+                }
+                double rowdot = 0.0; /* sum_j P_ij dP_ij */
+                for (int64_t t = 0; t < nk; t++) {
+                    p[t] /= L;
+                    const int64_t vo = ((b * N + keys[t]) * Hkv + kh) * D;
+                    double d = 0.0;
+                    for (int64_t c = 0; c < D; c++)
+                        d += load_elem(dout, dtype, qo + c) * load_elem(v, dtype, vo + c);
+                    dp[t] = d;
+                    rowdot += p[t] * d;
+                }
+                for (int64_t c = 0; c < D; c++) dq[qo + c] = 0.0;
+                for (int64_t t = 0; t < nk; t++) {
+                    const int64_t ko = ((b * N + keys[t]) * Hkv + kh) * D;
+                    const double ds = p[t] * (dp[t] - rowdot);
+                    for (int64_t c = 0; c < D; c++) {
+                        dq[qo + c] += scale * ds * load_elem(k, dtype, ko + c);
+                        dk[ko + c] += scale * ds * load_elem(q, dtype, qo + c);
+                        dv[ko + c] += p[t] * load_elem(dout, dtype, qo + c);
+                    }
+                }
+            }
+    free(keys);
+    free(p);
+    free(dp);
+    free(G);
+    return 0;
+}
+
 /* ---- ring-buffer KV cache -------------------------------------------- */
 
 /* Appends k_new, v_new [B,Hkv,D] into kcache, vcache [B,Hkv,W,D] (element type

@@ -543,10 +543,103 @@ def pin_paged_equals_ring(orc):
         _close(l1, l2, 1e-12, f"paged vs ring lse at {p0}")
 
 
+# ---- backward ----------------------------------------------------------------------
+
+BWD_CASES = [
+    # (B, Hq, Hkv, N, D, wl, wr, dil, globals, dtype, scale)
+    (1, 2, 2, 23, 8, 5, 0, 1, None, "f32", 0.4),            # causal
+    (2, 4, 2, 31, 8, 3, 6, 1, None, "bf16", None),          # asymmetric bidirectional, GQA
+    (1, 2, 1, 40, 8, 4, 0, 3, None, "bf16", 0.3),           # dilated causal, GQA 2
+    (1, 2, 2, 33, 8, 2, 2, 1, [0, 9, 32], "f32", None),     # bidirectional + globals
+    (1, 2, 2, 30, 8, 3, 0, 2, [4, 5, 17], "f32", 0.5),      # dilated causal + globals
+]
+
+
+def _torch_grads(q, k, v, dout, wl, wr, dil, G, scale):
+    """Gradients by torch autograd (float64, CPU) of the dense-masked attention."""
+    qf, kf, vf, gf = (torch.from_numpy(bruteforce.widen(x)) for x in (q, k, v, dout))
+    qf.requires_grad_(True)
+    kf.requires_grad_(True)
+    vf.requires_grad_(True)
+    Hq, Hkv, N = q.shape[2], k.shape[2], q.shape[1]
+    rep = Hq // Hkv
+    allowed = torch.from_numpy(bruteforce.mask_matrix(N, wl, wr, dil, G))
+    kr = kf.repeat_interleave(rep, dim=2)
+    vr = vf.repeat_interleave(rep, dim=2)
+    s = scale * torch.einsum("bihd,bjhd->bhij", qf, kr)
+    s = s.masked_fill(~allowed, float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), vr)
+    (o * gf).sum().backward()
+    return qf.grad.numpy(), kf.grad.numpy(), vf.grad.numpy()
+
+
+def pin_bwd_autograd(orc):
+    """Oracle gradients equal torch autograd through the dense-masked softmax."""
+    for n, (B, Hq, Hkv, N, D, wl, wr, dil, G, dt, sc) in enumerate(BWD_CASES):
+        q, k, v = fwd_inputs(400 + n, B, Hq, Hkv, N, D, dt)
+        dout = fwd_inputs(450 + n, B, Hq, Hkv, N, D, dt)[0]
+        scale = sc if sc is not None else 1 / math.sqrt(D)
+        dq, dk, dv = orc.bwd(q, k, v, dout, win_left=wl, win_right=wr, dilation=dil,
+                             global_idx=G, scale=scale)
+        tq, tk, tv = _torch_grads(q, k, v, dout, wl, wr, dil, G, scale)
+        _close(dq, tq, 1e-10, f"bwd case {n} dq")
+        _close(dk, tk, 1e-10, f"bwd case {n} dk")
+        _close(dv, tv, 1e-10, f"bwd case {n} dv")
+
+
+def pin_bwd_finite_differences(orc):
+    """Directional derivatives of L = sum(dout * out) by central differences of
+    the oracle's own forward (step 2^-12 on exactly representable inputs)."""
+    B, Hq, Hkv, N, D, wl, wr, dil, G = 1, 2, 1, 9, 4, 2, 1, 1, [7]
+    q, k, v = fwd_inputs(460, B, Hq, Hkv, N, D, "f32")
+    q, k, v = (np.round(x * 64) / 64 for x in (q, k, v))      # room for exact steps
+    q, k, v = (x.astype(np.float32) for x in (q, k, v))
+    dout = fwd_inputs(461, B, Hq, Hkv, N, D, "f32")[0]
+    dq, dk, dv = orc.bwd(q, k, v, dout, win_left=wl, win_right=wr, dilation=dil, global_idx=G,
+                         scale=0.7)
+    rng = np.random.Generator(np.random.PCG64(462))
+    h = 2.0 ** -12
+
+    def loss(q_, k_, v_):
+        o, _ = orc.fwd(q_, k_, v_, win_left=wl, win_right=wr, dilation=dil, global_idx=G,
+                       scale=0.7)
+        return float(np.sum(o * dout))
+
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(3):
+            u = rng.integers(-1, 2, size=x.shape).astype(np.float32)   # entries in {-1, 0, 1}
+            args = {"q": q, "k": k, "v": v}
+            args[name] = x + h * u
+            fp = loss(args["q"], args["k"], args["v"])
+            args[name] = x - h * u
+            fm = loss(args["q"], args["k"], args["v"])
+            fd = (fp - fm) / (2 * h)
+            an = float(np.sum(g * u))
+            assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, fd, an)
+
+
+def pin_bwd_closed_forms(orc):
+    """A zero window: each query sees only itself, so P = 1, dq = dk = 0 and
+    dv_i = the sum of dout_i over the kv head's query heads.  In general the
+    dv rows of a kv head sum to the dout rows of its query heads (each row of
+    P sums to 1)."""
+    B, Hq, Hkv, N, D = 1, 4, 2, 13, 8
+    q, k, v = fwd_inputs(470, B, Hq, Hkv, N, D, "bf16")
+    dout = fwd_inputs(471, B, Hq, Hkv, N, D, "bf16")[0]
+    dq, dk, dv = orc.bwd(q, k, v, dout, win_left=0, win_right=0)
+    g = bruteforce.widen(dout).reshape(B, N, Hkv, Hq // Hkv, D).sum(axis=3)
+    _close(dq, 0.0 * dq, 0.0, "zero window dq")
+    _close(dk, 0.0 * dk, 0.0, "zero window dk")
+    _close(dv, g, 1e-12, "zero window dv")
+    dq, dk, dv = orc.bwd(q, k, v, dout, win_left=4, win_right=2, dilation=2, global_idx=[3])
+    _close(dv.sum(axis=1), g.sum(axis=1), 1e-10, "dv rows sum to dout rows")
+
+
 ALL_PINS = [
     pin_dilated_index_sets, pin_dilated_span, pin_edge_truncation, pin_decode_demo_window,
     pin_ring_buffer_trace, pin_bruteforce, pin_bruteforce_mask_is_page_mask, pin_full_window,
     pin_zero_window, pin_q_zero, pin_dilation_strided, pin_gqa, pin_globals, pin_decode,
     pin_append_chunk, pin_chunked_prefill, pin_prefill_then_decode, pin_decode_sinks,
-    pin_paged_stream, pin_paged_equals_ring,
+    pin_paged_stream, pin_paged_equals_ring, pin_bwd_autograd, pin_bwd_finite_differences,
+    pin_bwd_closed_forms,
 ]

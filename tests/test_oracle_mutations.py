@@ -73,6 +73,16 @@ MUTATIONS = {
     "paged_window_short": ("pos = seq_len[bb] > W ? seq_len[bb] - W : 0;",
                            "pos = seq_len[bb] > W ? seq_len[bb] - W + 1 : 0;"),
     "paged_count_not_advanced": ("        seq_len[b] += n;", "        seq_len[b] += n - (n > 1);"),
+    "bwd_drop_row_term": ("const double ds = p[t] * (dp[t] - rowdot);",
+                          "const double ds = p[t] * dp[t];"),
+    "bwd_dq_no_scale": ("dq[qo + c] += scale * ds * load_elem(k, dtype, ko + c);",
+                        "dq[qo + c] += ds * load_elem(k, dtype, ko + c);"),
+    "bwd_dv_uses_ds": ("dv[ko + c] += p[t] * load_elem(dout, dtype, qo + c);",
+                       "dv[ko + c] += ds * load_elem(dout, dtype, qo + c);"),
+    "bwd_dk_uses_k": ("dk[ko + c] += scale * ds * load_elem(q, dtype, qo + c);",
+                      "dk[ko + c] += scale * ds * load_elem(k, dtype, ko + c);"),
+    "bwd_dp_uses_k": ("d += load_elem(dout, dtype, qo + c) * load_elem(v, dtype, vo + c);",
+                      "d += load_elem(dout, dtype, qo + c) * load_elem(k, dtype, vo + c);"),
 }
 
 
