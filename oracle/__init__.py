@@ -97,6 +97,12 @@ class OracleLib:
         lib.oracle_bwd.argtypes = [P, P, P, P, I, I64, I64, I64, I64, I64, I64, I64, I64, P,
                                    I64, D, P, P, P]
         lib.oracle_bwd.restype = I
+        lib.oracle_bwd_dq_rows.argtypes = [P, P, P, P, I, I64, I64, I64, I64, I64, I64, I64,
+                                           I64, P, I64, D, P, I64, P]
+        lib.oracle_bwd_dq_rows.restype = I
+        lib.oracle_bwd_dkv_keys.argtypes = [P, P, P, P, I, I64, I64, I64, I64, I64, I64, I64,
+                                            I64, P, I64, D, P, I64, P, P]
+        lib.oracle_bwd_dkv_keys.restype = I
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = I
         self.lib = lib
@@ -185,6 +191,46 @@ class OracleLib:
         if rc != 0:
             raise ValueError("invalid arguments to oracle_bwd")
         return dq, dk, dv
+
+    def _bwd_args(self, q, k, v, dout, scale, global_idx):
+        q, dt = _as_input(q)
+        k, _ = _as_input(k)
+        v, _ = _as_input(v)
+        dout, _ = _as_input(dout)
+        B, N, Hq, D = q.shape
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        g, ng = _globals(global_idx)
+        return q, k, v, dout, dt, B, N, Hq, k.shape[2], D, float(scale), g, ng
+
+    def bwd_dq_rows(self, q, k, v, dout, rows, *, win_left: int, win_right: int = 0,
+                    dilation: int = 1, global_idx=None, scale=None):
+        """dq of the rows (b, h, i) listed in rows [R,3] -> [R,D] float64."""
+        q, k, v, dout, dt, B, N, Hq, Hkv, D, scale, g, ng = self._bwd_args(
+            q, k, v, dout, scale, global_idx)
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        out = np.zeros((rows.shape[0], D), np.float64)
+        rc = self.lib.oracle_bwd_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, B, Hq, Hkv,
+                                         N, D, win_left, win_right, dilation, _ptr(g), ng, scale,
+                                         _ptr(rows), rows.shape[0], _ptr(out))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_bwd_dq_rows")
+        return out
+
+    def bwd_dkv_keys(self, q, k, v, dout, keys, *, win_left: int, win_right: int = 0,
+                     dilation: int = 1, global_idx=None, scale=None):
+        """(dk, dv) of the keys (b, kv head, j) listed in keys [R,3] -> two [R,D]."""
+        q, k, v, dout, dt, B, N, Hq, Hkv, D, scale, g, ng = self._bwd_args(
+            q, k, v, dout, scale, global_idx)
+        keys = np.ascontiguousarray(np.asarray(keys, dtype=np.int64).reshape(-1, 3))
+        dk = np.zeros((keys.shape[0], D), np.float64)
+        dv = np.zeros((keys.shape[0], D), np.float64)
+        rc = self.lib.oracle_bwd_dkv_keys(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), dt, B, Hq, Hkv,
+                                          N, D, win_left, win_right, dilation, _ptr(g), ng,
+                                          scale, _ptr(keys), keys.shape[0], _ptr(dk), _ptr(dv))
+        if rc != 0:
+            raise ValueError("invalid arguments to oracle_bwd_dkv_keys")
+        return dk, dv
 
     def ring(self, kcache, vcache, ring_head, cache_len) -> "Ring":
         return Ring(self, kcache, vcache, ring_head, cache_len)
@@ -349,6 +395,14 @@ def fwd_rows(*a, **kw):
 
 def bwd(*a, **kw):
     return default().bwd(*a, **kw)
+
+
+def bwd_dq_rows(*a, **kw):
+    return default().bwd_dq_rows(*a, **kw)
+
+
+def bwd_dkv_keys(*a, **kw):
+    return default().bwd_dkv_keys(*a, **kw)
 
 
 def ring(*a, **kw) -> Ring:

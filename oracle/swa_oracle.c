@@ -313,6 +313,160 @@ int oracle_bwd(const void* q, const void* k, const void* v, const void* dout, in
     return 0;
 }
 
+/* Softmax weights and dP of one query row over its attended set: fills
+ * keys[0..n), p (normalised weights) and dp; returns n and the row term
+ * sum_j p_j dp_j in *rowdot.  Helper of the sampled backward below. */
+static int64_t bwd_row(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                       int64_t b, int64_t h, int64_t i, int64_t N, int64_t Hq, int64_t Hkv,
+                       int64_t D, int64_t wl, int64_t wr, int64_t dil, const int64_t* G,
+                       int64_t nG, double scale, int64_t* keys, double* p, double* dp,
+                       double* rowdot) {
+    const int64_t kh = h / (Hq / Hkv);
+    const int64_t nk = attended_set(i, N, wl, wr, dil, G, nG, keys);
+    const int64_t qo = ((b * N + i) * Hq + h) * D;
+    double M = -INFINITY;
+    for (int64_t t = 0; t < nk; t++) {
+        const int64_t ko = ((b * N + keys[t]) * Hkv + kh) * D;
+        double dot = 0.0, g = 0.0;
+        for (int64_t c = 0; c < D; c++) {
+            dot += load_elem(q, dtype, qo + c) * load_elem(k, dtype, ko + c);
+            g += load_elem(dout, dtype, qo + c) * load_elem(v, dtype, ko + c);
+        }
+        p[t] = scale * dot;
+        dp[t] = g;
+        if (p[t] > M) M = p[t];
+    }
+    double L = 0.0;
+    for (int64_t t = 0; t < nk; t++) {
+        p[t] = exp(p[t] - M);
+        L += p[t];
+    }
+    double rd = 0.0;
+    for (int64_t t = 0; t < nk; t++) {
+        p[t] /= L;
+        rd += p[t] * dp[t];
+    }
+    *rowdot = rd;
+    return nk;
+}
+
+/* dq of the listed query rows (b, h, i) only: out_rows[r*D .. r*D+D-1]. */
+int oracle_bwd_dq_rows(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                       int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int64_t wl,
+                       int64_t wr, int64_t dil, const int32_t* gidx, int64_t ng, double scale,
+                       const int64_t* rows, int64_t n_rows, double* out_rows) {
+    if (!fwd_args_ok(B, Hq, Hkv, N, D, wl, wr, dil, dtype)) return -1;
+    for (int64_t t = 0; t < ng; t++)
+        if (gidx[t] < 0 || gidx[t] >= N) return -1;
+    for (int64_t r = 0; r < n_rows; r++)
+        if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 ||
+            rows[3 * r + 1] >= Hq || rows[3 * r + 2] < 0 || rows[3 * r + 2] >= N)
+            return -1;
+    int64_t* G = (int64_t*)malloc(sizeof(int64_t) * (size_t)(ng > 0 ? ng : 1));
+    int64_t nG = normalise_globals(gidx, ng, G);
+#pragma omp parallel
+    {
+        const size_t cap = (size_t)(N + wl + wr + nG + 1);
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * cap);
+        double* p = (double*)malloc(sizeof(double) * cap);
+        double* dp = (double*)malloc(sizeof(double) * cap);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; r++) {
+            const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+            double rowdot;
+            const int64_t nk = bwd_row(q, k, v, dout, dtype, b, h, i, N, Hq, Hkv, D, wl, wr, dil,
+                                       G, nG, scale, keys, p, dp, &rowdot);
+            double* o = out_rows + r * D;
+            for (int64_t c = 0; c < D; c++) o[c] = 0.0;
+            const int64_t kh = h / (Hq / Hkv);
+            for (int64_t t = 0; t < nk; t++) {
+                const int64_t ko = ((b * N + keys[t]) * Hkv + kh) * D;
+                const double dsq = p[t] * (dp[t] - rowdot);
+                for (int64_t c = 0; c < D; c++) o[c] += scale * dsq * load_elem(k, dtype, ko + c);
+            }
+        }
+        free(keys);
+        free(p);
+        free(dp);
+    }
+    free(G);
+    return 0;
+}
+
+/* dk and dv of the listed keys (b, kv head, j) only: every query row i of the
+ * kv head's query heads whose attended set holds j contributes; rows are
+ * scanned over [0, N) (the set test decides).  dk_rows, dv_rows [r*D ..]. */
+int oracle_bwd_dkv_keys(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, int64_t wl,
+                        int64_t wr, int64_t dil, const int32_t* gidx, int64_t ng, double scale,
+                        const int64_t* sel, int64_t n_sel, double* dk_rows, double* dv_rows) {
+    if (!fwd_args_ok(B, Hq, Hkv, N, D, wl, wr, dil, dtype)) return -1;
+    for (int64_t t = 0; t < ng; t++)
+        if (gidx[t] < 0 || gidx[t] >= N) return -1;
+    for (int64_t r = 0; r < n_sel; r++)
+        if (sel[3 * r] < 0 || sel[3 * r] >= B || sel[3 * r + 1] < 0 || sel[3 * r + 1] >= Hkv ||
+            sel[3 * r + 2] < 0 || sel[3 * r + 2] >= N)
+            return -1;
+    int64_t* G = (int64_t*)malloc(sizeof(int64_t) * (size_t)(ng > 0 ? ng : 1));
+    int64_t nG = normalise_globals(gidx, ng, G);
+    const int64_t group = Hq / Hkv;
+    for (int64_t r = 0; r < n_sel; r++) {
+        double* dkr = dk_rows + r * D;
+        double* dvr = dv_rows + r * D;
+        for (int64_t c = 0; c < D; c++) dkr[c] = dvr[c] = 0.0;
+    }
+    for (int64_t r = 0; r < n_sel; r++) {
+        const int64_t b = sel[3 * r], kh = sel[3 * r + 1], j = sel[3 * r + 2];
+        double* dkr = dk_rows + r * D;
+        double* dvr = dv_rows + r * D;
+#pragma omp parallel
+        {
+            const size_t cap = (size_t)(N + wl + wr + nG + 1);
+            int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * cap);
+            double* p = (double*)malloc(sizeof(double) * cap);
+            double* dp = (double*)malloc(sizeof(double) * cap);
+            double* dk_l = (double*)calloc((size_t)D, sizeof(double));
+            double* dv_l = (double*)calloc((size_t)D, sizeof(double));
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t x = 0; x < group * N; x++) {
+                const int64_t h = kh * group + x / N, i = x % N;
+                /* cheap pre-test: is j in S(i)?  (globals make any row possible) */
+                int64_t ks_tmp_n;
+                int in = 0;
+                {
+                    const int64_t dj = j - i;
+                    if (dj % dil == 0 && dj / dil >= -wl && dj / dil <= wr) in = 1;
+                }
+                if (!in && nG == 0) continue;
+                double rowdot;
+                ks_tmp_n = bwd_row(q, k, v, dout, dtype, b, h, i, N, Hq, Hkv, D, wl, wr, dil, G,
+                                   nG, scale, keys, p, dp, &rowdot);
+                for (int64_t t = 0; t < ks_tmp_n; t++) {
+                    if (keys[t] != j) continue;
+                    const int64_t qo = ((b * N + i) * Hq + h) * D;
+                    const double dsk = p[t] * (dp[t] - rowdot);
+                    for (int64_t c = 0; c < D; c++) {
+                        dk_l[c] += scale * dsk * load_elem(q, dtype, qo + c);
+                        dv_l[c] += p[t] * load_elem(dout, dtype, qo + c);
+                    }
+                }
+            }
+#pragma omp critical
+            for (int64_t c = 0; c < D; c++) {
+                dkr[c] += dk_l[c];
+                dvr[c] += dv_l[c];
+            }
+            free(keys);
+            free(p);
+            free(dp);
+            free(dk_l);
+            free(dv_l);
+        }
+    }
+    free(G);
+    return 0;
+}
+
 /* ---- ring-buffer KV cache -------------------------------------------- */
 
 /* Appends k_new, v_new [B,Hkv,D] into kcache, vcache [B,Hkv,W,D] (element type

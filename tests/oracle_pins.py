@@ -635,11 +635,29 @@ def pin_bwd_closed_forms(orc):
     _close(dv.sum(axis=1), g.sum(axis=1), 1e-10, "dv rows sum to dout rows")
 
 
+def pin_bwd_sampled(orc):
+    """The row- and key-sampled backward entry points agree with the full one."""
+    for n, (B, Hq, Hkv, N, D, wl, wr, dil, G, dt, sc) in enumerate(BWD_CASES[:4]):
+        q, k, v = fwd_inputs(400 + n, B, Hq, Hkv, N, D, dt)
+        dout = fwd_inputs(450 + n, B, Hq, Hkv, N, D, dt)[0]
+        kw = dict(win_left=wl, win_right=wr, dilation=dil, global_idx=G, scale=sc)
+        dq, dk, dv = orc.bwd(q, k, v, dout, **kw)
+        rows = np.array([[0, 0, 0], [B - 1, Hq - 1, N - 1], [0, Hq // 2, N // 2]])
+        got = orc.bwd_dq_rows(q, k, v, dout, rows, **kw)
+        for r, (b, h, i) in enumerate(rows):
+            _close(got[r], dq[b, i, h], 1e-12, f"sampled dq case {n}")
+        sel = np.array([[0, 0, 0], [B - 1, Hkv - 1, N - 1], [0, Hkv - 1, N // 3]])
+        gk, gv = orc.bwd_dkv_keys(q, k, v, dout, sel, **kw)
+        for r, (b, kh, j) in enumerate(sel):
+            _close(gk[r], dk[b, j, kh], 1e-12, f"sampled dk case {n}")
+            _close(gv[r], dv[b, j, kh], 1e-12, f"sampled dv case {n}")
+
+
 ALL_PINS = [
     pin_dilated_index_sets, pin_dilated_span, pin_edge_truncation, pin_decode_demo_window,
     pin_ring_buffer_trace, pin_bruteforce, pin_bruteforce_mask_is_page_mask, pin_full_window,
     pin_zero_window, pin_q_zero, pin_dilation_strided, pin_gqa, pin_globals, pin_decode,
     pin_append_chunk, pin_chunked_prefill, pin_prefill_then_decode, pin_decode_sinks,
     pin_paged_stream, pin_paged_equals_ring, pin_bwd_autograd, pin_bwd_finite_differences,
-    pin_bwd_closed_forms,
+    pin_bwd_closed_forms, pin_bwd_sampled,
 ]

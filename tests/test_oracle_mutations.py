@@ -83,6 +83,10 @@ MUTATIONS = {
                       "dk[ko + c] += scale * ds * load_elem(k, dtype, ko + c);"),
     "bwd_dp_uses_k": ("d += load_elem(dout, dtype, qo + c) * load_elem(v, dtype, vo + c);",
                       "d += load_elem(dout, dtype, qo + c) * load_elem(k, dtype, vo + c);"),
+    "bwd_rows_drop_row_term": ("const double dsq = p[t] * (dp[t] - rowdot);",
+                               "const double dsq = p[t] * dp[t];"),
+    "bwd_keys_dv_uses_ds": ("dv_l[c] += p[t] * load_elem(dout, dtype, qo + c);",
+                            "dv_l[c] += dsk * load_elem(dout, dtype, qo + c);"),
 }
 
 
