@@ -314,6 +314,46 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
                      float scale, void* workspace, size_t workspace_bytes, int dtype,
                      hipStream_t stream);
 
+/*
+ * swa_bwd: gradients of swa_fwd (training use: bmjup.com "Sliding window
+ * attention", Q&A on training vs inference; intelliparadigm.com section 5.1,
+ * blocked and mixed-precision training).  For the upstream gradient dout of
+ * out, with P_ij the forward's attention weights over S(i) and
+ * dP_ij = dout_i . v_j:
+ *   dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij')
+ *   dq_i = scale sum_j dS_ij k_j;  dk_j = scale sum_i dS_ij q_i;  dv_j = sum_i P_ij dout_i
+ * (a kv head collects the terms of every query head of its group).  P is
+ * rebuilt from the forward's lse, so out and lse must come from swa_fwd with
+ * the same arguments.  In bf16, P and dS are rounded to bf16 before their
+ * products, as the forward rounds its weights.
+ *
+ *   q, k, v, out, dout   device, layouts and dtype of swa_fwd (dout like out)
+ *   lse                  device, [B, Hq, N] float32 from swa_fwd (required)
+ *   dq                   device, [B, N, Hq, D] of `dtype` (written)
+ *   dk, dv               device, [B, N, Hkv, D] of `dtype` (written; keys no
+ *                        query attends get 0)
+ *   win_left, win_right, dilation, scale   as for swa_fwd
+ *   global_idx, n_global must describe no global token (n_global == 0):
+ *                        the backward of global tokens is not provided
+ *   workspace            device scratch of swa_bwd_workspace_size() bytes
+ *                        (per-row dout . out); two calls in flight at once
+ *                        must not share it
+ *
+ * Errors: as swa_fwd (with lse, dout, dq, dk, dv required), plus
+ * SWA_ERR_UNSUPPORTED when n_global > 0 and SWA_ERR_WORKSPACE for a missing
+ * or short workspace.
+ */
+int swa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv,
+            int B, int Hq, int Hkv, int N, int D,
+            int win_left, int win_right, int dilation,
+            const int32_t* global_idx, int n_global,
+            float scale, int dtype,
+            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace swa_bwd needs (0 on bad sizes). */
+size_t swa_bwd_workspace_size(int B, int Hq, int N, int D);
+
 /* A static, human-readable description of a status code. */
 const char* swa_status_string(int status);
 

@@ -8,5 +8,5 @@ call does, and fails loudly if it has not been built.
 from .binding import (  # noqa: F401
     SwaError, fwd, fwd_workspace_size, fwd_cached, kv_append, kv_append_chunk, decode,
     decode_workspace_size, decode_sinks, decode_sinks_workspace_size, kv_append_paged,
-    decode_paged, load_library,
+    decode_paged, bwd, bwd_workspace_size, load_library,
 )

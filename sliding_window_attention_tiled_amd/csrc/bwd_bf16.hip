@@ -1,0 +1,489 @@
+// bwd_bf16.hip -- backward of the sliding-window attention forward, bf16
+// inputs, gfx950 MFMA.
+//
+// The gradients follow from the chain rule through s = scale q.k, the softmax
+// over the attended set and the weighted sum of v (training with windowed
+// attention: bmjup.com "Sliding window attention", Q&A on training vs
+// inference; intelliparadigm.com section 5.1).  With P_ij = exp2(s_ij c -
+// lse2_i) rebuilt from the forward's log-sum-exp, dP_ij = dout_i . v_j and
+// delta_i = dout_i . out_i (= sum_j P_ij dP_ij):
+//   dS_ij = P_ij (dP_ij - delta_i)
+//   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
+// Three launches, no atomics:
+//   1. delta per query row;
+//   2. query-major (the forward's work items and key tiles): S^T = K Q^T,
+//      dP^T = V dout^T, then dq^T += K^T dS^T, with K^T read transposed from
+//      the K tile;
+//   3. key-major: a workgroup owns 128 keys of one kv head and walks the query
+//      positions whose windows reach them, for every query head of the group:
+//      S = Q K^T and dP = dout V^T with keys on the lanes, then
+//      dv^T += dout^T P and dk^T += Q^T dS, with dout^T and Q^T read
+//      transposed from LDS.
+// Both passes rebuild P from lse instead of a running softmax, so a key tile
+// needs no rescaling.  P and dS enter the MFMAs rounded to bf16.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "fwd_common.h"
+#include "swa_kernels.h"
+#include "tile_common.h"
+
+namespace swa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- 1. delta_i = dout_i . out_i ---------------------------------------------------
+// D/8 lanes per row (8 elements each), 256 threads.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const T* out, const T* dout, float* delta,
+                                                        int Hq, int N, int64_t rows) {
+    constexpr int LPR = D / 8;
+    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const T* o = out + row * D + part * 8;
+        const T* g = dout + row * D + part * 8;
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
+    if (row < rows && part == 0) {
+        // row = (b * N + i) * Hq + h  ->  delta[(b * Hq + h) * N + i]
+        const int h = (int)(row % Hq);
+        const int64_t bi = row / Hq;
+        const int64_t b = bi / N, i = bi % N;
+        delta[(b * Hq + h) * N + i] = acc;
+    }
+}
+
+// ---- 2. dq: query-major ----------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_bf16_kernel(const BwdParams bp) {
+    using T = TileCfg<D, NW>;
+    const FwdParams& p = bp.f;
+    constexpr int KC = D / 16;   // 16-deep k-steps of the D contractions
+    constexpr int DB = D / 32;   // 32-row blocks of dq^T
+
+    __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) int gk_lds[2][2 * BN];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+
+    const WorkItem wi = decode_band_item(p, xcd_contiguous(blockIdx.x, gridDim.x), BN);
+    const int b = wi.b, kvh = wi.kvh, hg = wi.hg;
+    const KeyStream& ks = wi.ks;
+    const int wave_row0 = wi.row0 + (wave / p.hpw) * 32;
+    const int hq = kvh * p.group + hg * p.hpw + (wave % p.hpw);
+
+    const int rowstride = p.Hkv * D;
+    const __bf16* kbase = (const __bf16*)p.k + ((size_t)b * p.N * p.Hkv + kvh) * D;
+    const __bf16* vbase = (const __bf16*)p.v + ((size_t)b * p.N * p.Hkv + kvh) * D;
+
+    // the lane's query row: q and dout as B operands, lse and delta
+    const int row = wave_row0 + l32;
+    const int qres = row;
+    const int qpos = row < ks.Nr ? ks.r + row * ks.dil : -1;
+    bf16x8 qreg[KC], greg[KC];
+    {
+        const size_t qo = (((size_t)b * p.N + max(qpos, 0)) * p.Hq + hq) * D + half * 8;
+        const __bf16* qp = (const __bf16*)p.q + qo;
+        const __bf16* gp = (const __bf16*)bp.dout + qo;
+        const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            qreg[kc] = qpos >= 0 ? *(const bf16x8*)(qp + kc * 16) : z;
+            greg[kc] = qpos >= 0 ? *(const bf16x8*)(gp + kc * 16) : z;
+        }
+    }
+    const size_t lrow = ((size_t)b * p.Hq + hq) * p.N + max(qpos, 0);
+    const float lse2 = qpos >= 0 ? p.lse[lrow] * kLog2e : 0.f;
+    const float dlt = qpos >= 0 ? bp.delta[lrow] : 0.f;
+    const int w_first = wave_row0;
+    const int w_last = min(wave_row0 + 31, ks.Nr - 1);
+
+    f32x16 dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) dqacc[db] = f32x16{};
+    const float c = p.scale_log2;
+
+    u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
+    if (ks.n_tiles > 0) {
+        load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, 0, gk_lds[0],
+                            nullptr);
+        store_tile<T>(kr, vr, smem);
+    }
+    __syncthreads();
+
+    const int key_l = half * 4 + ((lane & 15) >> 2);
+    const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    for (int j = 0; j < ks.n_tiles; j++) {
+        const int st = j & 1;
+        const bool has_next = j + 1 < ks.n_tiles;
+        const int kt0 = ks.k_lo + j * BN;
+        const int kt1 = kt0 + BN - 1;
+        const bool skip = w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl;
+        const bool need_mask = !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
+        const unsigned short* Ks = smem + st * T::STAGE;
+        const unsigned short* Vs = Ks + T::K_ELEMS;
+        f32x16 s[2], dp[2];
+        if (!skip) {
+            // S^T = K Q^T and dP^T = V dout^T: two 32-key blocks each
+            s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < KC; kc++) {
+                bf16x8 ka[2], va[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
+                    ka[kb] = *(const bf16x8*)(Ks + (kb * 32 + l32) * T::KP + kc * 16 + half * 8);
+                    va[kb] = *(const bf16x8*)(Vs + (kb * 32 + l32) * T::VP + kc * 16 + half * 8);
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qreg[kc], s[kb], 0, 0, 0);
+                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb], greg[kc], dp[kb], 0, 0, 0);
+                }
+            }
+        }
+        if (has_next)
+            load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, j + 1,
+                                gk_lds[st ^ 1], nullptr);
+        if (!skip) {
+            if (need_mask) {
+                // the forward's band edge masks (x = key - query + wl in [0, wl + wr],
+                // key <= k_hi), integer arithmetic
+                const int base = kt0 + half * 4 - qres + p.wl;
+                const int sb = p.wl + p.wr - base;
+                const int lim = ks.k_hi - kt0 - half * 4;
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
+                        const int bad = ((base + ko) | (sb - ko) | (lim - ko)) >> 31;
+                        s[kb][e] += __builtin_bit_cast(float, bad & 0xff800000);
+                    }
+            }
+            // dS^T = P^T (dP^T - delta), bf16, in the B-operand slot order of the
+            // forward's P^T; then dq^T += K^T dS^T over four 16-key steps
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                bf16x8 ds;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int ei = (t & 1) * 8 + e;
+                    const float pe = fast_exp2(__builtin_fmaf(s[t >> 1][ei], c, -lse2));
+                    ds[e] = (__bf16)(pe * (dp[t >> 1][ei] - dlt));
+                }
+#pragma unroll
+                for (int db = 0; db < DB; db++) {
+                    const unsigned short* kp = Ks + (t * 16 + key_l) * T::KP + db * 32 + col_l;
+                    const i16x4 lo = lds_read_tr16(kp);
+                    const i16x4 hi = lds_read_tr16(kp + 8 * T::KP);
+                    const bf16x8 ka = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ds, dqacc[db], 0, 0, 0);
+                }
+            }
+        }
+        if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
+        __syncthreads();
+    }
+
+    if (qpos < 0) return;
+    // dq^T block: element (db, jq*4 + e) is dim db*32 + jq*8 + half*4 + e of query l32
+    __bf16* op = (__bf16*)bp.dq + (((size_t)b * p.N + qpos) * p.Hq + hq) * D;
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int jq = 0; jq < 4; jq++) {
+            bf16x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o4[e] = (__bf16)(dqacc[db][jq * 4 + e] * bp.scale);
+            *(bf16x4*)(op + db * 32 + jq * 8 + half * 4) = o4;
+        }
+}
+
+// ---- 3. dk, dv: key-major ------------------------------------------------------------
+constexpr int BK = 128;   // keys per workgroup (four waves of 32)
+constexpr int BQ = 64;    // query rows per staged tile
+
+template <int D>
+struct QTileCfg {
+    static constexpr int QP = D + 8;                  // row pitch (bf16) of the Q and dout tiles
+    static constexpr int ELEMS = BQ * QP;
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    static constexpr int PER_THREAD = BQ * CPR / 256;
+    static constexpr int ROW_STEP = 256 / CPR;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams bp) {
+    using Q = QTileCfg<D>;
+    const FwdParams& p = bp.f;
+    constexpr int KC = D / 16;
+    constexpr int DB = D / 32;
+
+    // per stage: Q tile, dout tile, lse2[BQ], delta[BQ]
+    __shared__ __attribute__((aligned(16))) unsigned short qsm[2][2 * Q::ELEMS];
+    __shared__ __attribute__((aligned(16))) float rsm[2][2 * BQ];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+
+    // work item: (b, kv head, residue class, key block); blocks of a slab from
+    // the last to the first, as in the forward
+    const int L = xcd_contiguous(blockIdx.x, gridDim.x);
+    int t = bp.ktiles_per_slab - 1 - L % bp.ktiles_per_slab;
+    const int slab = L / bp.ktiles_per_slab;
+    const int kvh = slab % p.Hkv;
+    const int b = slab / p.Hkv;
+    int r, kt, Nr;
+    const int long_total = p.rem * bp.ktiles_long;
+    if (t < long_total) {
+        r = t / bp.ktiles_long;
+        kt = t % bp.ktiles_long;
+        Nr = p.qd + 1;
+    } else {
+        t -= long_total;
+        r = p.rem + t / bp.ktiles_short;
+        kt = t % bp.ktiles_short;
+        Nr = p.qd;
+    }
+    const int kb0 = kt * BK;
+    const int kb1 = min(kb0 + BK - 1, Nr - 1);
+    const int wk0 = kb0 + wave * 32;               // this wave's first key
+    const int wk1 = min(wk0 + 31, kb1);
+    // query rows whose windows reach the block: i - wl <= j <= i + wr
+    const int q_lo = max(0, kb0 - p.wr);
+    const int q_hi = min(Nr - 1, kb1 + p.wl);
+    const int n_qt = (q_hi - q_lo + BQ) / BQ;
+    const int n_steps = n_qt * p.group;            // (query head, query tile) pairs
+
+    // the lane's key as the B operand of S = Q K^T and dP = dout V^T
+    const int key = wk0 + l32;
+    const bool key_ok = key <= kb1;
+    const int kpos = r + min(key, kb1) * p.dil;
+    bf16x8 kreg[KC], vreg[KC];
+    {
+        const size_t ko = (((size_t)b * p.N + kpos) * p.Hkv + kvh) * D + half * 8;
+        const __bf16* kp = (const __bf16*)p.k + ko;
+        const __bf16* vp = (const __bf16*)p.v + ko;
+        const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            kreg[kc] = key_ok ? *(const bf16x8*)(kp + kc * 16) : z;
+            vreg[kc] = key_ok ? *(const bf16x8*)(vp + kc * 16) : z;
+        }
+    }
+    f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; db++) dkacc[db] = dvacc[db] = f32x16{};
+    const float c = p.scale_log2;
+    const int span = p.wl + p.wr;
+
+    // staging of step st: query head h = st / n_qt, tile qt = st % n_qt
+    u32x4 qr[Q::PER_THREAD], gr[Q::PER_THREAD];
+    float rl = 0.f;
+    auto load_step = [&](int st) {
+        const int hq = kvh * p.group + st / n_qt;
+        const int q0 = q_lo + (st % n_qt) * BQ;
+        const int row0 = threadIdx.x / Q::CPR, cc = threadIdx.x % Q::CPR;
+#pragma unroll
+        for (int u = 0; u < Q::PER_THREAD; u++) {
+            const int qrow = q0 + row0 + u * Q::ROW_STEP;
+            if (qrow <= q_hi) {
+                const size_t off =
+                    (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
+                qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
+                gr[u] = *(const u32x4*)((const __bf16*)bp.dout + off);
+            } else {
+                qr[u] = gr[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        // lse (base 2) for threads 0..63, delta for 64..127, one row each
+        if (threadIdx.x < 2 * BQ) {
+            const int qrow = q0 + (threadIdx.x & (BQ - 1));
+            rl = 0.f;
+            if (qrow <= q_hi) {
+                const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
+                rl = threadIdx.x < BQ ? p.lse[li] * kLog2e : bp.delta[li];
+            }
+        }
+    };
+    auto store_step = [&](int stage) {
+        const int row0 = threadIdx.x / Q::CPR, cc = threadIdx.x % Q::CPR;
+        unsigned short* qs = qsm[stage];
+        unsigned short* gs = qs + Q::ELEMS;
+#pragma unroll
+        for (int u = 0; u < Q::PER_THREAD; u++) {
+            const int rw = row0 + u * Q::ROW_STEP;
+            *(u32x4*)(qs + rw * Q::QP + cc * 8) = qr[u];
+            *(u32x4*)(gs + rw * Q::QP + cc * 8) = gr[u];
+        }
+        if (threadIdx.x < 2 * BQ) rsm[stage][threadIdx.x] = rl;
+    };
+
+    if (n_steps > 0) {
+        load_step(0);
+        store_step(0);
+    }
+    __syncthreads();
+    const int key_l = half * 4 + ((lane & 15) >> 2);
+    const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    for (int st = 0; st < n_steps; st++) {
+        const int stage = st & 1;
+        const bool has_next = st + 1 < n_steps;
+        const int q0 = q_lo + (st % n_qt) * BQ;
+        const int q1 = q0 + BQ - 1;
+        // wave-uniform: no pair of this wave's keys with these queries / all pairs valid
+        const bool skip = wk0 > kb1 || q0 > wk1 + p.wl || q1 < wk0 - p.wr;
+        const bool need_mask = !(q0 >= wk1 - p.wr && q1 <= wk0 + p.wl && q1 <= q_hi &&
+                                 wk0 + 31 <= kb1);
+        const unsigned short* Qs = qsm[stage];
+        const unsigned short* Gs = Qs + Q::ELEMS;
+        const float* lse2 = rsm[stage];
+        const float* dlt = lse2 + BQ;
+        f32x16 s[2], dp[2];
+        if (!skip) {
+            // S = Q K^T and dP = dout V^T: two 32-query row blocks, keys on the lanes
+            s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+            for (int kc = 0; kc < KC; kc++) {
+                bf16x8 qa[2], ga[2];
+#pragma unroll
+                for (int rb = 0; rb < 2; rb++) {
+                    qa[rb] = *(const bf16x8*)(Qs + (rb * 32 + l32) * Q::QP + kc * 16 + half * 8);
+                    ga[rb] = *(const bf16x8*)(Gs + (rb * 32 + l32) * Q::QP + kc * 16 + half * 8);
+                }
+#pragma unroll
+                for (int rb = 0; rb < 2; rb++) {
+                    s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb], kreg[kc], s[rb], 0, 0, 0);
+                    dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[rb], vreg[kc], dp[rb], 0, 0, 0);
+                }
+            }
+        }
+        if (has_next) load_step(st + 1);
+        if (!skip) {
+            if (need_mask) {
+                // element (rb, e) is query q0 + rb*32 + (e>>2)*8 + half*4 + (e&3) and key
+                // `key`: valid when x = query - key + wr lies in [0, wl + wr], the query
+                // is <= q_hi and the key <= kb1
+#pragma unroll
+                for (int rb = 0; rb < 2; rb++) {
+                    const int base = q0 + rb * 32 + half * 4 - key + p.wr;
+                    const int qlim = q_hi - (q0 + rb * 32 + half * 4);
+                    const int kbad = kb1 - key;
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int ro = (e >> 2) * 8 + (e & 3);
+                        const int bad = ((base + ro) | (span - base - ro) | (qlim - ro) | kbad) >> 31;
+                        s[rb][e] += __builtin_bit_cast(float, bad & 0xff800000);
+                    }
+                }
+            }
+            // P and dS in bf16, B-operand slot order; then dv^T += dout^T P and
+            // dk^T += Q^T dS over four 16-query steps
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const int rb = t >> 1;
+                const int rowb = rb * 32 + (t & 1) * 16 + half * 4;   // rows of slots 0..3
+                const f32x4 l_lo = *(const f32x4*)(lse2 + rowb);
+                const f32x4 l_hi = *(const f32x4*)(lse2 + rowb + 8);
+                const f32x4 d_lo = *(const f32x4*)(dlt + rowb);
+                const f32x4 d_hi = *(const f32x4*)(dlt + rowb + 8);
+                bf16x8 pb, dsb;
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int ei = (t & 1) * 8 + e;
+                    const float l2 = e < 4 ? l_lo[e] : l_hi[e - 4];
+                    const float dl = e < 4 ? d_lo[e] : d_hi[e - 4];
+                    const float pe = fast_exp2(__builtin_fmaf(s[rb][ei], c, -l2));
+                    pb[e] = (__bf16)pe;
+                    dsb[e] = (__bf16)(pe * (dp[rb][ei] - dl));
+                }
+#pragma unroll
+                for (int db = 0; db < DB; db++) {
+                    const unsigned short* gp = Gs + (t * 16 + key_l) * Q::QP + db * 32 + col_l;
+                    const unsigned short* qp = Qs + (t * 16 + key_l) * Q::QP + db * 32 + col_l;
+                    const i16x4 glo = lds_read_tr16(gp), ghi = lds_read_tr16(gp + 8 * Q::QP);
+                    const i16x4 qlo = lds_read_tr16(qp), qhi = lds_read_tr16(qp + 8 * Q::QP);
+                    const bf16x8 ga = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const bf16x8 qa = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, dvacc[db], 0, 0, 0);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb, dkacc[db], 0, 0, 0);
+                }
+            }
+        }
+        if (has_next) store_step(stage ^ 1);
+        __syncthreads();
+    }
+
+    if (!key_ok) return;
+    const size_t ko = (((size_t)b * p.N + kpos) * p.Hkv + kvh) * D;
+    __bf16* dkp = (__bf16*)bp.dk + ko;
+    __bf16* dvp = (__bf16*)bp.dv + ko;
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int jq = 0; jq < 4; jq++) {
+            bf16x4 k4, v4;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                k4[e] = (__bf16)(dkacc[db][jq * 4 + e] * bp.scale);
+                v4[e] = (__bf16)dvacc[db][jq * 4 + e];
+            }
+            *(bf16x4*)(dkp + db * 32 + jq * 8 + half * 4) = k4;
+            *(bf16x4*)(dvp + db * 32 + jq * 8 + half * 4) = v4;
+        }
+}
+
+template <int D, typename T>
+hipError_t launch_delta(const BwdParams& p, hipStream_t s) {
+    const int64_t rows = (int64_t)p.f.B * p.f.N * p.f.Hq;
+    const int64_t dblocks = (rows * (D / 8) + 255) / 256;
+    if (dblocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((bwd_delta_kernel<D, T>), dim3((unsigned)dblocks), dim3(256), 0, s,
+                       (const T*)p.out, (const T*)p.dout, p.delta, p.f.Hq, p.f.N, rows);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, 4>), dim3(p.f.n_blocks), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D>), dim3(p.k_blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+FwdShape bwd_bf16_dq_shape(int group) {
+    // four waves: the heads of a GQA group that share the K/V tiles, times rows
+    const int hpw = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+    const int rows = (4 / hpw) * 32;
+    return FwdShape{hpw, rows, rows};
+}
+
+int bwd_bf16_dkdv_keys() { return BK; }
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t s) {
+    return D == 128 ? launch_d<128>(p, s) : launch_d<64>(p, s);
+}
+
+hipError_t launch_bwd_delta(const BwdParams& p, int D, int dtype, hipStream_t s) {
+    if (dtype == SWA_BF16) return D == 128 ? launch_delta<128, __bf16>(p, s) : launch_delta<64, __bf16>(p, s);
+    return D == 128 ? launch_delta<128, float>(p, s) : launch_delta<64, float>(p, s);
+}
+
+}  // namespace swa

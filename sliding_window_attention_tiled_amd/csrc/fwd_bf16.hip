@@ -38,120 +38,13 @@
 #include "device_common.h"
 #include "fwd_common.h"
 #include "swa_kernels.h"
+#include "tile_common.h"
 
 
 namespace swa {
 namespace {
 
-constexpr int BN = 64;        // keys per K/V tile
 constexpr int kQB = 1;  // 32-query blocks per wave
-constexpr int kFarAway = -(1 << 30);  // residue coordinate outside every window
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int D, int NW>
-struct TileCfg {
-    static constexpr int NT = 64 * NW;                          // threads per workgroup
-    // LDS row pitches (bf16 elements).  K rows are read 16 B per lane, 16
-    // rows per LDS cycle: a pitch of 4 (mod 64) dwords puts those rows on
-    // distinct banks.  V rows are read by ds_read_b64_tr_b16, 4 rows x 64 B per
-    // 32 lanes: a pitch of 16 (mod 64) dwords keeps those on distinct banks.
-    static constexpr int KP = D + 8;
-    static constexpr int VP = ((D + 95) / 128) * 128 + 32;       // = 32 (mod 128)
-    static constexpr int K_ELEMS = BN * KP;
-    static constexpr int V_ELEMS = BN * VP;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int CPR = D / 8;                            // 16-byte chunks per row
-    static constexpr int PER_THREAD = BN * CPR / NT;
-    static constexpr int KEY_STEP = NT / CPR;                    // rows between a thread's chunks
-    static_assert(PER_THREAD * NT == BN * CPR, "tile does not split evenly");
-};
-
-// Loads tile j of the key stream into registers (zero rows for padding).
-// For gathered global-key tiles it also records, per key, the position and
-// the residue coordinate g / d when g is in this residue class (else a value
-// no window reaches) in gk[2][BN], for the element masks.  Band tiles that
-// start at a negative coordinate (chunked prefill) take those keys from the
-// ring rows krbase / vrbase (row pitch D).
-template <class T, bool GROWS>
-__device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
-                                          u32x4 (&vr)[T::PER_THREAD],
-                                          const __bf16* kbase, const __bf16* vbase,
-                                          const __bf16* krbase, const __bf16* vrbase,
-                                          int rowstride, const KeyStream& ks, const FwdParams& p,
-                                          int j, int* gk, const int* gpos) {
-    const int key0 = threadIdx.x / T::CPR;
-    const int c = threadIdx.x % T::CPR;
-    if (!GROWS && j < ks.n_band_tiles && ks.k_lo + j * BN < 0) {
-        // d = 1 and r = 0 here: coordinate = position within the chunk
-        const int kk0 = ks.k_lo + j * BN + key0;
-#pragma unroll
-        for (int u = 0; u < T::PER_THREAD; u++) {
-            const int kk = kk0 + u * T::KEY_STEP;
-            const __bf16* ks_src = nullptr;
-            const __bf16* vs_src = nullptr;
-            if (kk < 0) {
-                const size_t off = (size_t)ring_slot(ks, kk, p.W) * T::CPR * 8 + c * 8;
-                ks_src = krbase + off;
-                vs_src = vrbase + off;
-            } else if (kk <= ks.k_hi) {
-                const size_t off = (size_t)kk * rowstride + c * 8;
-                ks_src = kbase + off;
-                vs_src = vbase + off;
-            }
-            kr[u] = ks_src ? *(const u32x4*)ks_src : u32x4{0u, 0u, 0u, 0u};
-            vr[u] = vs_src ? *(const u32x4*)vs_src : u32x4{0u, 0u, 0u, 0u};
-        }
-        return;
-    }
-    int kpos[T::PER_THREAD];
-    if (GROWS || j < ks.n_band_tiles) {
-        const int kk0 = ks.k_lo + j * BN + key0;
-#pragma unroll
-        for (int u = 0; u < T::PER_THREAD; u++) {
-            const int kk = kk0 + u * T::KEY_STEP;
-            kpos[u] = kk <= ks.k_hi ? ks.r + kk * ks.dil : -1;
-        }
-    } else {
-        const int g0 = (j - ks.n_band_tiles) * BN + key0;
-#pragma unroll
-        for (int u = 0; u < T::PER_THREAD; u++) {
-            const int gi = g0 + u * T::KEY_STEP;
-            kpos[u] = gi < ks.n_global ? gpos[gi] : -1;
-            if (c == 0) {
-                const int g = kpos[u];
-                gk[key0 + u * T::KEY_STEP] = g;
-                gk[BN + key0 + u * T::KEY_STEP] =
-                    (g >= 0 && g % ks.dil == ks.r) ? g / ks.dil : kFarAway;
-            }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < T::PER_THREAD; u++) {
-        if (kpos[u] >= 0) {
-            const size_t off = (size_t)kpos[u] * rowstride + c * 8;
-            kr[u] = *(const u32x4*)(kbase + off);
-            vr[u] = *(const u32x4*)(vbase + off);
-        } else {
-            kr[u] = u32x4{0u, 0u, 0u, 0u};
-            vr[u] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
-template <class T>
-__device__ __forceinline__ void store_tile(const u32x4 (&kr)[T::PER_THREAD],
-                                           const u32x4 (&vr)[T::PER_THREAD],
-                                           unsigned short* stage) {
-    const int key0 = threadIdx.x / T::CPR;
-    const int c = threadIdx.x % T::CPR;
-#pragma unroll
-    for (int u = 0; u < T::PER_THREAD; u++) {
-        const int key = key0 + u * T::KEY_STEP;
-        *(u32x4*)(stage + key * T::KP + c * 8) = kr[u];
-        *(u32x4*)(stage + T::K_ELEMS + key * T::VP + c * 8) = vr[u];
-    }
-}
 
 // GROWS = false: band workgroups (plus global key columns).
 // GROWS = true : global query rows over one key chunk, partial output.

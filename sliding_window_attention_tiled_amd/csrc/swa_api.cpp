@@ -44,11 +44,9 @@ void decode_splits(int B, int Hq, int W, int* splits, int* per_split) {
 
 // Band work decomposition of a forward launch (p.B, Hkv, group, N, dil set).
 // False when the grid would not fit in 32 bits.
-bool plan_band(FwdParams& p, int dtype, swa::FwdShape* shape_out) {
+bool plan_band_shape(FwdParams& p, const swa::FwdShape& shape) {
     p.qd = p.N / p.dil;
     p.rem = p.N % p.dil;
-    const swa::FwdShape shape =
-        dtype == SWA_BF16 ? swa::fwd_bf16_shape(p.group) : swa::fwd_f32_shape(p.group);
     p.hpw = shape.hpw;
     p.bmq = shape.bmq;
     p.head_groups = p.group / p.hpw;
@@ -60,8 +58,12 @@ bool plan_band(FwdParams& p, int dtype, swa::FwdShape* shape_out) {
     if (per_slab > INT32_MAX || blocks > INT32_MAX) return false;
     p.tiles_per_slab = (int)per_slab;
     p.n_blocks = (int)blocks;
-    *shape_out = shape;
     return true;
+}
+
+bool plan_band(FwdParams& p, int dtype, swa::FwdShape* shape_out) {
+    *shape_out = dtype == SWA_BF16 ? swa::fwd_bf16_shape(p.group) : swa::fwd_f32_shape(p.group);
+    return plan_band_shape(p, *shape_out);
 }
 
 // Merges the split partials of a decode launch into out / lse.
@@ -364,6 +366,69 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
                                      : swa::launch_decode_f32(p, D, true, stream);
     if (e != hipSuccess) return SWA_ERR_HIP;
     return combine_decode(p, out, lse, D, dtype, stream);
+}
+
+size_t swa_bwd_workspace_size(int B, int Hq, int N, int D) {
+    if (B <= 0 || Hq <= 0 || N <= 0 || N > kMaxN || !supported_d(D)) return 0;
+    return ((size_t)B * Hq * N * sizeof(float) + 255) / 256 * 256;
+}
+
+int swa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+            const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int D,
+            int win_left, int win_right, int dilation, const int32_t* global_idx, int n_global,
+            float scale, int dtype, void* workspace, size_t workspace_bytes,
+            hipStream_t stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return SWA_ERR_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || N > kMaxN || D <= 0) return SWA_ERR_ARG;
+    if (Hq % Hkv != 0) return SWA_ERR_ARG;
+    if (win_left < 0 || win_right < 0 || dilation < 1) return SWA_ERR_ARG;
+    if (n_global < 0 || (n_global > 0 && !global_idx)) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    if (n_global > 0) return SWA_ERR_UNSUPPORTED;  // global tokens: forward only
+    if (!workspace || workspace_bytes < swa_bwd_workspace_size(B, Hq, N, D))
+        return SWA_ERR_WORKSPACE;
+
+    swa::BwdParams bp;
+    std::memset(&bp, 0, sizeof bp);
+    FwdParams& p = bp.f;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lse = const_cast<float*>(lse);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.N = N;
+    p.group = Hq / Hkv;
+    p.causal = win_right == 0;
+    p.wl = std::min(win_left, N);
+    p.wr = std::min(win_right, N);
+    p.dil = dilation;
+    p.scale_log2 = scale * kLog2e;
+    const swa::FwdShape shape =
+        dtype == SWA_BF16 ? swa::bwd_bf16_dq_shape(p.group) : swa::bwd_f32_dq_shape(p.group);
+    if (!plan_band_shape(p, shape)) return SWA_ERR_ARG;
+    bp.out = out;
+    bp.dout = dout;
+    bp.delta = (float*)workspace;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.scale = scale;
+    bp.bmk = dtype == SWA_BF16 ? swa::bwd_bf16_dkdv_keys() : swa::bwd_f32_dkdv_keys();
+    bp.ktiles_long = (int)cdiv(p.qd + 1, bp.bmk);
+    bp.ktiles_short = (int)cdiv(p.qd, bp.bmk);
+    const int64_t per_slab =
+        (int64_t)p.rem * bp.ktiles_long + (int64_t)(dilation - p.rem) * bp.ktiles_short;
+    const int64_t kblocks = (int64_t)B * Hkv * per_slab;
+    if (per_slab > INT32_MAX || kblocks > INT32_MAX) return SWA_ERR_ARG;
+    bp.ktiles_per_slab = (int)per_slab;
+    bp.k_blocks = (int)kblocks;
+
+    if (swa::launch_bwd_delta(bp, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
+    hipError_t e = dtype == SWA_BF16 ? swa::launch_bwd_bf16(bp, D, stream)
+                                     : swa::launch_bwd_f32(bp, D, stream);
+    return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
 }
 
 }  // extern "C"

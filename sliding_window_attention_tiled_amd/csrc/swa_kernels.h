@@ -59,6 +59,25 @@ struct FwdParams {
     int W;
 };
 
+// One backward launch: the forward's band plan (no global tokens) in f, plus
+// the upstream gradient, the forward's lse, the per-row dot(dout, out) and
+// the gradient outputs.  The key-major pass tiles each residue class's keys
+// in blocks of bmk and visits the query positions whose windows reach them.
+struct BwdParams {
+    FwdParams f;
+    const void* out;
+    const void* dout;
+    float* delta;      // [B][Hq][N]: sum_d dout * out per query row
+    void* dq;
+    void* dk;
+    void* dv;
+    float scale;       // multiplier of q.k (dq, dk carry it)
+    int bmk;                        // keys per key-major workgroup
+    int ktiles_long, ktiles_short;  // key blocks in a long / short residue class
+    int ktiles_per_slab;            // key blocks of one (b, kv head)
+    int k_blocks;                   // grid of the key-major pass
+};
+
 struct DecodeParams {
     const void* q;
     const void* kcache;
@@ -107,6 +126,13 @@ FwdShape fwd_f32_shape(int group);
 // Launchers (return hipError_t of the launch).
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
+FwdShape bwd_bf16_dq_shape(int group);
+int bwd_bf16_dkdv_keys();
+FwdShape bwd_f32_dq_shape(int group);
+int bwd_f32_dkdv_keys();
+hipError_t launch_bwd_delta(const BwdParams& p, int D, int dtype, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn,
                             int32_t* head, int32_t* len, int B, int Hkv, int W, int D,
                             int elem_bytes, hipStream_t s);

@@ -33,7 +33,8 @@ def test_header_declares_entry_points():
     for n in ["swa_fwd", "swa_fwd_workspace_size", "swa_kv_append", "swa_decode",
               "swa_decode_workspace_size", "swa_status_string", "swa_version",
               "swa_kv_append_chunk", "swa_fwd_cached", "swa_decode_sinks",
-              "swa_decode_sinks_workspace_size", "swa_kv_append_paged", "swa_decode_paged"]:
+              "swa_decode_sinks_workspace_size", "swa_kv_append_paged", "swa_decode_paged",
+              "swa_bwd", "swa_bwd_workspace_size"]:
         assert n in names
 
 
@@ -239,3 +240,27 @@ def test_paged_validation(lib):
     assert dec(Hq=6, Hkv=4) == ARG and dec(P=12) == ARG and dec(nb=7) == ARG
     assert dec(D=80) == UNSUP
     assert dec(ws=None) == WS and dec(wsb=need - 1) == WS
+
+
+def test_bwd_validation(lib):
+    f = lib.swa_bwd
+    names = ["q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "B", "Hq", "Hkv", "N", "D",
+             "wl", "wr", "dil", "g", "ng", "scale", "dtype", "ws", "wsb", "stream"]
+    need = lib.swa_bwd_workspace_size(1, 4, 128, 128)
+    assert need >= 4 * 128 * 4 and lib.swa_bwd_workspace_size(1, 4, 128, 96) == 0
+    base = [P, P, P, P, P, P, P, P, P, 1, 4, 2, 128, 128, 7, 0, 1, None, 0, 0.1, 1, P, need,
+            None]
+
+    def call(**ch):
+        a = list(base)
+        for k_, v_ in ch.items():
+            a[names.index(k_)] = v_
+        return f(*a)
+    for ptr in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert call(**{ptr: None}) == ARG, ptr
+    assert call(Hq=6, Hkv=4) == ARG and call(wl=-1) == ARG and call(dil=0) == ARG
+    assert call(N=(1 << 28) + 1) == ARG
+    assert call(D=80) == UNSUP and call(dtype=5) == UNSUP
+    g = (ctypes.c_int32 * 2)(0, 5)
+    assert call(g=g, ng=2) == UNSUP                     # no backward of global tokens
+    assert call(ws=None) == WS and call(wsb=need - 1) == WS
