@@ -12,7 +12,8 @@ K+V streamed, and the fp64 CPU oracle timed on a bounded sample of rows.
 Also reported, per call: the bidirectional encoder with global tokens, the
 four layers of the dilated stack and one 4096-token chunk of a chunked prefill
 (exact TFLOP/s against min(MFMA peak, HBM peak x arithmetic intensity)), and
-the decode shape with four attention sinks and through a paged pool (GB/s).
+the decode shape with four attention sinks and through a paged pool (GB/s),
+and the backward of the headline layer (TFLOP/s at 10*D flop per pair).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
                     [--no-others]
@@ -36,6 +37,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
 FWD_SOURCES = ["sliding_window_attention_tiled_amd/csrc/fwd_bf16.hip",
+               "sliding_window_attention_tiled_amd/csrc/tile_common.h",
                "sliding_window_attention_tiled_amd/csrc/fwd_common.h",
                "sliding_window_attention_tiled_amd/csrc/device_common.h",
                "sliding_window_attention_tiled_amd/csrc/swa_kernels.h"]
@@ -312,7 +314,34 @@ def bench_other_workloads():
                         "append_chunk_gbs": round(append_bytes / (ams * 1e-3) / 1e9, 1)}))
     del q, k, v, kc, vc, kc2, vc2, out, lse
     res.extend(bench_decode_variants())
+    res.append(bench_bwd())
     return res
+
+
+def bench_bwd():
+    """Backward of the Mistral-shaped causal layer (config of the headline):
+    one swa_bwd call (delta, dq pass, dk/dv pass).  Algorithmic work 10*D flop
+    per attended pair (recomputed q.k, dP, dv, dk, dq: 2*D each); the kernels
+    execute 14*D (the query-major and key-major passes each form q.k and dP)."""
+    import torch
+    from sliding_window_attention_tiled_amd import binding, configs
+    from sliding_window_attention_tiled_amd.inputs import fwd_inputs
+
+    c = configs.FWD["mistral_causal_w4096"]
+    B, Hq, Hkv, N, D = c["B"], c["Hq"], c["Hkv"], c["N"], c["D"]
+    W = c["win_left"] + 1
+    q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], B, Hq, Hkv, N, D, c["dtype"]))
+    g = to_dev(fwd_inputs(c["seed"] + 100, B, Hq, Hkv, N, D, c["dtype"])[0])
+    out, lse = binding.fwd(q, k, v, win_left=c["win_left"])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(binding.bwd_workspace_size(B, Hq, N, D), dtype=torch.uint8, device="cuda")
+    ms, mn = _time_calls(lambda: binding.bwd(q, k, v, out, lse, g, win_left=c["win_left"],
+                                             dq=dq, dk=dk, dv=dv, workspace=ws))
+    pairs = exact_pairs_causal(N, W)
+    flop = 10.0 * B * Hq * D * pairs
+    bytes_ = (4.0 * B * N * Hq * D + 4.0 * B * N * Hkv * D) * 2 + 8.0 * B * Hq * N
+    return _report("bwd_mistral_causal_w4096", ms, mn, flop, bytes_,
+                   {"flop_per_pair": "10*D algorithmic (14*D executed)"})
 
 
 def _decode_report(name, ms, ms_min, kv_bytes, extra=None):
