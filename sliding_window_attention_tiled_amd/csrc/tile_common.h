@@ -71,15 +71,21 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
         }
         return;
     }
-    int kpos[T::PER_THREAD];
     if (GROWS || j < ks.n_band_tiles) {
+        // band keys past k_hi only occur in the last tile, which is always
+        // element-masked: load them from k_hi instead of predicating the loads
         const int kk0 = ks.k_lo + j * BN + key0;
 #pragma unroll
         for (int u = 0; u < T::PER_THREAD; u++) {
-            const int kk = kk0 + u * T::KEY_STEP;
-            kpos[u] = kk <= ks.k_hi ? ks.r + kk * ks.dil : -1;
+            const int kk = min(kk0 + u * T::KEY_STEP, ks.k_hi);
+            const size_t off = (size_t)(ks.r + kk * ks.dil) * rowstride + c * 8;
+            kr[u] = *(const u32x4*)(kbase + off);
+            vr[u] = *(const u32x4*)(vbase + off);
         }
-    } else {
+        return;
+    }
+    int kpos[T::PER_THREAD];
+    {
         const int g0 = (j - ks.n_band_tiles) * BN + key0;
 #pragma unroll
         for (int u = 0; u < T::PER_THREAD; u++) {
