@@ -24,13 +24,18 @@ SOURCES = ["swa_api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16
 
 # Packed FP32 instructions stay off: every float operation is scalar per lane.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device flags.  The backward kernels keep loop-carried MFMA
+# accumulators: in the VGPR form the compiler feeds them to the matrix cores
+# where they live instead of copying them through the AGPR file on every step.
+SOURCE_FLAGS = {"bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-I", os.path.join(PKG, "..", "include")]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = SOURCE_FLAGS.get(src, [])
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o",
                obj]

@@ -60,8 +60,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* out, const T* d
 }
 
 // ---- 2. dq: query-major ----------------------------------------------------------
+// Two workgroups per CU: the register cap of 128 costs a few spills, which the
+// second resident workgroup more than hides.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_bf16_kernel(const BwdParams bp) {
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams bp) {
     using T = TileCfg<D, NW>;
     const FwdParams& p = bp.f;
     constexpr int KC = D / 16;   // 16-deep k-steps of the D contractions
@@ -355,19 +357,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
         if (!skip) {
             // S = Q K^T and dP = dout V^T: two 32-query row blocks, keys on the lanes
             s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+            // two k-steps of fragments at a time: reading every fragment ahead
+            // would need more registers than the lane has
 #pragma unroll
-            for (int kc = 0; kc < KC; kc++) {
-                bf16x8 qa[2], ga[2];
+            for (int kc = 0; kc < KC; kc += 2) {
+                bf16x8 qa[2][2], ga[2][2];
 #pragma unroll
-                for (int rb = 0; rb < 2; rb++) {
-                    qa[rb] = *(const bf16x8*)(Qs + (rb * 32 + l32) * Q::QP + kc * 16 + half * 8);
-                    ga[rb] = *(const bf16x8*)(Gs + (rb * 32 + l32) * Q::QP + kc * 16 + half * 8);
-                }
+                for (int u = 0; u < 2; u++)
 #pragma unroll
-                for (int rb = 0; rb < 2; rb++) {
-                    s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb], kreg[kc], s[rb], 0, 0, 0);
-                    dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[rb], vreg[kc], dp[rb], 0, 0, 0);
-                }
+                    for (int rb = 0; rb < 2; rb++) {
+                        const int off = (rb * 32 + l32) * Q::QP + (kc + u) * 16 + half * 8;
+                        qa[u][rb] = *(const bf16x8*)(Qs + off);
+                        ga[u][rb] = *(const bf16x8*)(Gs + off);
+                    }
+#pragma unroll
+                for (int u = 0; u < 2; u++)
+#pragma unroll
+                    for (int rb = 0; rb < 2; rb++) {
+                        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u][rb], kreg[kc + u],
+                                                                        s[rb], 0, 0, 0);
+                        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[u][rb], vreg[kc + u],
+                                                                         dp[rb], 0, 0, 0);
+                    }
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then MFMAs
             }
         }
         if (has_next) load_step(st + 1);
@@ -422,6 +435,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
                     dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, dvacc[db], 0, 0, 0);
                     dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb, dkacc[db], 0, 0, 0);
                 }
+                // this step's transposed reads, then its MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);
             }
         }
         if (has_next) store_step(stage ^ 1);
