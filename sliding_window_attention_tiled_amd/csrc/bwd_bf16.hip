@@ -23,6 +23,8 @@
 // needs no rescaling.  P and dS enter the MFMAs rounded to bf16.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "fwd_common.h"
 #include "swa_kernels.h"
@@ -32,6 +34,31 @@ namespace swa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Transposed operands (K^T in the dq pass, dout^T and Q^T in the dk/dv pass)
+// are read with ds_read_b64_tr_b16 from tiles whose row pitch is 4 (mod 64)
+// dwords, the pitch that keeps the 16-byte row reads of the same tiles free of
+// bank conflicts.  In one such read, 32 lanes fetch 4 rows x 8 chunks of 8
+// bytes.  Taking the rows {0, 1, 8, 9} of a 16-row step (the high read: 2 rows
+// further) and chunks at dword offsets {0, 2, 8, 10, 16, 18, 24, 26} places
+// the 32 chunks on 64 distinct banks.  The B operand's k slots follow the same
+// row order (slot_elem), and the accumulator rows follow the chunks (acc_dim).
+__device__ __forceinline__ int tr_row(int lane) {
+    const int e4 = (lane & 15) >> 2;
+    return (lane >> 5) * 4 + (e4 & 1) + (e4 >> 1) * 8;
+}
+__device__ __forceinline__ int tr_col(int lane) {
+    const int c = lane & 3;
+    return 32 * ((lane >> 4) & 1) + 16 * (c >> 1) + 4 * (c & 1);
+}
+constexpr int tr_block_col(int db) { return 8 * (db & 1) + 64 * (db >> 1); }
+constexpr int kTrHi = 2;
+// element (0..7 of a 16-row step of an MFMA result block) that fills B slot e
+constexpr int slot_elem(int e) { return (e & 1) | ((e & 2) << 1) | ((e & 4) >> 1); }
+// head dimension of accumulator element 4 * jq + e of block db on lane half h
+__device__ __forceinline__ int acc_dim(int db, int jq, int h) {
+    return tr_block_col(db) + 16 * jq + 4 * h;
+}
 
 // ---- 1. delta_i = dout_i . out_i ---------------------------------------------------
 // D/8 lanes per row (8 elements each), 256 threads.
@@ -60,11 +87,20 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* out, const T* d
 }
 
 // ---- 2. dq: query-major ----------------------------------------------------------
-// Two workgroups per CU: the register cap of 128 costs a few spills, which the
-// second resident workgroup more than hides.
+// The dq pass reads V by rows only (dP^T = V dout^T), so its V tile takes the K
+// tile's pitch.
+template <int D, int NW>
+struct DqTileCfg : TileCfg<D, NW> {
+    static constexpr int VP = TileCfg<D, NW>::KP;
+    static constexpr int V_ELEMS = BN * VP;
+    static constexpr int STAGE = TileCfg<D, NW>::K_ELEMS + V_ELEMS;
+};
+
+// Two workgroups per CU: the cap of 256 registers per lane costs a few spills,
+// which the second resident workgroup more than hides.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams bp) {
-    using T = TileCfg<D, NW>;
+    using T = DqTileCfg<D, NW>;
     const FwdParams& p = bp.f;
     constexpr int KC = D / 16;   // 16-deep k-steps of the D contractions
     constexpr int DB = D / 32;   // 32-row blocks of dq^T
@@ -122,8 +158,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
     }
     __syncthreads();
 
-    const int key_l = half * 4 + ((lane & 15) >> 2);
-    const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int tr_off = tr_row(lane) * T::KP + tr_col(lane);
     for (int j = 0; j < ks.n_tiles; j++) {
         const int st = j & 1;
         const bool has_next = j + 1 < ks.n_tiles;
@@ -171,22 +206,22 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
                         s[kb][e] += __builtin_bit_cast(float, bad & 0xff800000);
                     }
             }
-            // dS^T = P^T (dP^T - delta), bf16, in the B-operand slot order of the
-            // forward's P^T; then dq^T += K^T dS^T over four 16-key steps
+            // dS^T = P^T (dP^T - delta), bf16, in the slot order of the K^T reads;
+            // then dq^T += K^T dS^T over four 16-key steps
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 bf16x8 ds;
 #pragma unroll
                 for (int e = 0; e < 8; e++) {
-                    const int ei = (t & 1) * 8 + e;
+                    const int ei = (t & 1) * 8 + slot_elem(e);
                     const float pe = fast_exp2(__builtin_fmaf(s[t >> 1][ei], c, -lse2));
                     ds[e] = (__bf16)(pe * (dp[t >> 1][ei] - dlt));
                 }
 #pragma unroll
                 for (int db = 0; db < DB; db++) {
-                    const unsigned short* kp = Ks + (t * 16 + key_l) * T::KP + db * 32 + col_l;
+                    const unsigned short* kp = Ks + tr_off + t * 16 * T::KP + tr_block_col(db);
                     const i16x4 lo = lds_read_tr16(kp);
-                    const i16x4 hi = lds_read_tr16(kp + 8 * T::KP);
+                    const i16x4 hi = lds_read_tr16(kp + kTrHi * T::KP);
                     const bf16x8 ka = __builtin_bit_cast(
                         bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ds, dqacc[db], 0, 0, 0);
@@ -198,7 +233,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
     }
 
     if (qpos < 0) return;
-    // dq^T block: element (db, jq*4 + e) is dim db*32 + jq*8 + half*4 + e of query l32
+    // dq^T block: element (db, jq*4 + e) is dim acc_dim(db, jq, half) + e of query l32
     __bf16* op = (__bf16*)bp.dq + (((size_t)b * p.N + qpos) * p.Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < DB; db++)
@@ -207,7 +242,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
             bf16x4 o4;
 #pragma unroll
             for (int e = 0; e < 4; e++) o4[e] = (__bf16)(dqacc[db][jq * 4 + e] * bp.scale);
-            *(bf16x4*)(op + db * 32 + jq * 8 + half * 4) = o4;
+            *(bf16x4*)(op + acc_dim(db, jq, half)) = o4;
         }
 }
 
@@ -224,16 +259,63 @@ struct QTileCfg {
     static constexpr int ROW_STEP = 256 / CPR;
 };
 
+// Fragments of one 16-deep k-step of S = Q K^T and dP = dout V^T: the two
+// 32-query row blocks of Q and of dout (A operands, 16 bytes per lane).
+template <int D>
+struct ScoreFrag {
+    bf16x8 q[2], g[2];
+};
+template <int D>
+__device__ __forceinline__ ScoreFrag<D> read_score_frag(const unsigned short* Qs, int kc,
+                                                        int l32, int half) {
+    using Q = QTileCfg<D>;
+    ScoreFrag<D> f;
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+        const int off = (rb * 32 + l32) * Q::QP + kc * 16 + half * 8;
+        f.q[rb] = *(const bf16x8*)(Qs + off);
+        f.g[rb] = *(const bf16x8*)(Qs + Q::ELEMS + off);
+    }
+    return f;
+}
+
+// Transposed fragments of one 16-query step t: dout^T and Q^T for every
+// 32-row block of the head dimension.
+template <int D>
+struct TrFrag {
+    bf16x8 g[D / 32], q[D / 32];
+};
+template <int D>
+__device__ __forceinline__ TrFrag<D> read_tr_frag(const unsigned short* Qs, int tr_off, int t) {
+    using Q = QTileCfg<D>;
+    TrFrag<D> f;
+#pragma unroll
+    for (int db = 0; db < D / 32; db++) {
+        const int off = tr_off + t * 16 * Q::QP + tr_block_col(db);
+        const unsigned short* gp = Qs + Q::ELEMS + off;
+        const unsigned short* qp = Qs + off;
+        const i16x4 glo = lds_read_tr16(gp), ghi = lds_read_tr16(gp + kTrHi * Q::QP);
+        const i16x4 qlo = lds_read_tr16(qp), qhi = lds_read_tr16(qp + kTrHi * Q::QP);
+        f.g[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
+        f.q[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    return f;
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams bp) {
     using Q = QTileCfg<D>;
     const FwdParams& p = bp.f;
     constexpr int KC = D / 16;
     constexpr int DB = D / 32;
+    // Three LDS stages.  During step st the dk/dv products read tile st, the
+    // scores of step st + 1 read tile st + 1, and tile st + 2 is stored: the
+    // score MFMAs of the next step then run beside this step's exponentials.
+    constexpr int NS = 3;
 
     // per stage: Q tile, dout tile, lse2[BQ], delta[BQ]
-    __shared__ __attribute__((aligned(16))) unsigned short qsm[2][2 * Q::ELEMS];
-    __shared__ __attribute__((aligned(16))) float rsm[2][2 * BQ];
+    __shared__ __attribute__((aligned(16))) unsigned short qsm[NS][2 * Q::ELEMS];
+    __shared__ __attribute__((aligned(16))) float rsm[NS][2 * BQ];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -291,33 +373,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
     const float c = p.scale_log2;
     const int span = p.wl + p.wr;
 
-    // staging of step st: query head h = st / n_qt, tile qt = st % n_qt
+    // staging of step st (clamped to the last step, so a load past the end
+    // re-reads that step's rows): query head st / n_qt, tile st % n_qt.  Rows
+    // past q_hi take row q_hi's values: the element masks of such a tile (it
+    // always takes them) zero P and dS there, and the values are finite.
     u32x4 qr[Q::PER_THREAD], gr[Q::PER_THREAD];
     float rl = 0.f;
     auto load_step = [&](int st) {
+        st = min(st, n_steps - 1);
         const int hq = kvh * p.group + st / n_qt;
         const int q0 = q_lo + (st % n_qt) * BQ;
         const int row0 = threadIdx.x / Q::CPR, cc = threadIdx.x % Q::CPR;
 #pragma unroll
         for (int u = 0; u < Q::PER_THREAD; u++) {
-            const int qrow = q0 + row0 + u * Q::ROW_STEP;
-            if (qrow <= q_hi) {
-                const size_t off =
-                    (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
-                qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
-                gr[u] = *(const u32x4*)((const __bf16*)bp.dout + off);
-            } else {
-                qr[u] = gr[u] = u32x4{0u, 0u, 0u, 0u};
-            }
+            const int qrow = min(q0 + row0 + u * Q::ROW_STEP, q_hi);
+            const size_t off =
+                (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
+            qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
+            gr[u] = *(const u32x4*)((const __bf16*)bp.dout + off);
         }
         // lse (base 2) for threads 0..63, delta for 64..127, one row each
         if (threadIdx.x < 2 * BQ) {
-            const int qrow = q0 + (threadIdx.x & (BQ - 1));
-            rl = 0.f;
-            if (qrow <= q_hi) {
-                const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
-                rl = threadIdx.x < BQ ? p.lse[li] * kLog2e : bp.delta[li];
-            }
+            const int qrow = min(q0 + (int)(threadIdx.x & (BQ - 1)), q_hi);
+            const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
+            rl = threadIdx.x < BQ ? p.lse[li] * kLog2e : bp.delta[li];
         }
     };
     auto store_step = [&](int stage) {
@@ -333,115 +412,136 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
         if (threadIdx.x < 2 * BQ) rsm[stage][threadIdx.x] = rl;
     };
 
-    if (n_steps > 0) {
+    const int tr_off = tr_row(lane) * Q::QP + tr_col(lane);
+    f32x16 sc[2][2], dpc[2][2];   // scores and dP of two consecutive steps
+    // one k-step of S and dP into the set (s, dp)
+    auto scores = [&](f32x16 (&s)[2], f32x16 (&dp)[2], int kc, const ScoreFrag<D>& f) {
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.q[rb], kreg[kc], s[rb], 0, 0, 0);
+            dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.g[rb], vreg[kc], dp[rb], 0, 0, 0);
+        }
+    };
+    if (n_steps > 0) {   // uniform over the workgroup
         load_step(0);
         store_step(0);
+        load_step(1);
+        store_step(1);
+        __syncthreads();
+        sc[0][0] = sc[0][1] = dpc[0][0] = dpc[0][1] = f32x16{};
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++)
+            scores(sc[0], dpc[0], kc, read_score_frag<D>(qsm[0], kc, l32, half));
     }
-    __syncthreads();
-    const int key_l = half * 4 + ((lane & 15) >> 2);
-    const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    for (int st = 0; st < n_steps; st++) {
-        const int stage = st & 1;
-        const bool has_next = st + 1 < n_steps;
+
+    // One step: tile st in stage st % NS, its scores in set PAR.  The source
+    // order below is the issue order (the fences keep the compiler from
+    // regrouping it): the next step's score MFMAs, each k-step's fragments read
+    // one k-step ahead, with this step's P and dS computed between them; then
+    // the dk/dv MFMAs, each 16-query step's transposed fragments read one step
+    // ahead.
+    auto step = [&](int st, auto par_tag) {
+        constexpr int PAR = decltype(par_tag)::value;
+        const int stage = st % NS;
+        const int stage_next = (st + 1) % NS;
+        const int stage_store = (st + 2) % NS;
         const int q0 = q_lo + (st % n_qt) * BQ;
         const int q1 = q0 + BQ - 1;
-        // wave-uniform: no pair of this wave's keys with these queries / all pairs valid
-        const bool skip = wk0 > kb1 || q0 > wk1 + p.wl || q1 < wk0 - p.wr;
+        // wave-uniform: every pair of this wave's keys with these queries valid?
         const bool need_mask = !(q0 >= wk1 - p.wr && q1 <= wk0 + p.wl && q1 <= q_hi &&
                                  wk0 + 31 <= kb1);
+        f32x16 (&s)[2] = sc[PAR];
+        f32x16 (&dp)[2] = dpc[PAR];
+        if (need_mask) {
+            // element (rb, e) is query q0 + rb*32 + (e>>2)*8 + half*4 + (e&3) and key
+            // `key`: valid when x = query - key + wr lies in [0, wl + wr], the query
+            // is <= q_hi and the key <= kb1
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                const int base = q0 + rb * 32 + half * 4 - key + p.wr;
+                const int qlim = q_hi - (q0 + rb * 32 + half * 4);
+                const int kbad = kb1 - key;
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int ro = (e >> 2) * 8 + (e & 3);
+                    const int bad = ((base + ro) | (span - base - ro) | (qlim - ro) | kbad) >> 31;
+                    s[rb][e] += __builtin_bit_cast(float, bad & 0xff800000);
+                }
+            }
+        }
+        // next tile's rows into registers (stored at the end of the step)
+        load_step(st + 2);
         const unsigned short* Qs = qsm[stage];
-        const unsigned short* Gs = Qs + Q::ELEMS;
+        const unsigned short* Qn = qsm[stage_next];
         const float* lse2 = rsm[stage];
         const float* dlt = lse2 + BQ;
-        f32x16 s[2], dp[2];
-        if (!skip) {
-            // S = Q K^T and dP = dout V^T: two 32-query row blocks, keys on the lanes
-            s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-            // two k-steps of fragments at a time: reading every fragment ahead
-            // would need more registers than the lane has
+        f32x16 (&sn)[2] = sc[PAR ^ 1];
+        f32x16 (&dpn)[2] = dpc[PAR ^ 1];
+        sn[0] = sn[1] = dpn[0] = dpn[1] = f32x16{};
+
+        // phase 1: scores of step st + 1 (past the last step they read a stale
+        // stage and are never used) beside P and dS of step st, half a
+        // 16-query step per k-step
+        bf16x8 pb[4], dsb[4];
+        ScoreFrag<D> fr[2];
+        fr[0] = read_score_frag<D>(Qn, 0, l32, half);
+        f32x4 lr[4];   // lse2 rows 0..3 and 8..11 of the step, then delta's
 #pragma unroll
-            for (int kc = 0; kc < KC; kc += 2) {
-                bf16x8 qa[2][2], ga[2][2];
+        for (int kc = 0; kc < KC; kc++) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (kc + 1 < KC) fr[(kc + 1) & 1] = read_score_frag<D>(Qn, kc + 1, l32, half);
+            // this k-step's share of P and dS: elements g0 .. g0 + PER - 1 of the
+            // step's 32 (16-query step t, slots e0 ..)
+            constexpr int PER = 32 / KC;
+            const int g0 = kc * PER;
+            const int t = g0 / 8;
+            const int e0 = g0 % 8;
+            const int rowb = (t >> 1) * 32 + (t & 1) * 16 + half * 4;
+            if (e0 == 0) {
+                lr[0] = *(const f32x4*)(lse2 + rowb);
+                lr[1] = *(const f32x4*)(lse2 + rowb + 8);
+                lr[2] = *(const f32x4*)(dlt + rowb);
+                lr[3] = *(const f32x4*)(dlt + rowb + 8);
+            }
+            scores(sn, dpn, kc, fr[kc & 1]);
 #pragma unroll
-                for (int u = 0; u < 2; u++)
-#pragma unroll
-                    for (int rb = 0; rb < 2; rb++) {
-                        const int off = (rb * 32 + l32) * Q::QP + (kc + u) * 16 + half * 8;
-                        qa[u][rb] = *(const bf16x8*)(Qs + off);
-                        ga[u][rb] = *(const bf16x8*)(Gs + off);
-                    }
-#pragma unroll
-                for (int u = 0; u < 2; u++)
-#pragma unroll
-                    for (int rb = 0; rb < 2; rb++) {
-                        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[u][rb], kreg[kc + u],
-                                                                        s[rb], 0, 0, 0);
-                        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[u][rb], vreg[kc + u],
-                                                                         dp[rb], 0, 0, 0);
-                    }
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // then MFMAs
+            for (int i = 0; i < PER; i++) {
+                const int e = e0 + i;
+                const int el = slot_elem(e);          // row rowb + (el>>2)*8 + (el&3)
+                const int ei = (t & 1) * 8 + el;
+                const float l2 = lr[el >> 2][el & 3];
+                const float dl = lr[2 + (el >> 2)][el & 3];
+                const float pe = fast_exp2(__builtin_fmaf(s[t >> 1][ei], c, -l2));
+                pb[t][e] = (__bf16)pe;
+                dsb[t][e] = (__bf16)(pe * (dp[t >> 1][ei] - dl));
             }
         }
-        if (has_next) load_step(st + 1);
-        if (!skip) {
-            if (need_mask) {
-                // element (rb, e) is query q0 + rb*32 + (e>>2)*8 + half*4 + (e&3) and key
-                // `key`: valid when x = query - key + wr lies in [0, wl + wr], the query
-                // is <= q_hi and the key <= kb1
+        __builtin_amdgcn_sched_barrier(0);
+
+        // phase 2: dv^T += dout^T P and dk^T += Q^T dS over four 16-query steps
+        TrFrag<D> tf[2];
+        tf[0] = read_tr_frag<D>(Qs, tr_off, 0);
 #pragma unroll
-                for (int rb = 0; rb < 2; rb++) {
-                    const int base = q0 + rb * 32 + half * 4 - key + p.wr;
-                    const int qlim = q_hi - (q0 + rb * 32 + half * 4);
-                    const int kbad = kb1 - key;
+        for (int t = 0; t < 4; t++) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (t + 1 < 4) tf[(t + 1) & 1] = read_tr_frag<D>(Qs, tr_off, t + 1);
 #pragma unroll
-                    for (int e = 0; e < 16; e++) {
-                        const int ro = (e >> 2) * 8 + (e & 3);
-                        const int bad = ((base + ro) | (span - base - ro) | (qlim - ro) | kbad) >> 31;
-                        s[rb][e] += __builtin_bit_cast(float, bad & 0xff800000);
-                    }
-                }
-            }
-            // P and dS in bf16, B-operand slot order; then dv^T += dout^T P and
-            // dk^T += Q^T dS over four 16-query steps
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const int rb = t >> 1;
-                const int rowb = rb * 32 + (t & 1) * 16 + half * 4;   // rows of slots 0..3
-                const f32x4 l_lo = *(const f32x4*)(lse2 + rowb);
-                const f32x4 l_hi = *(const f32x4*)(lse2 + rowb + 8);
-                const f32x4 d_lo = *(const f32x4*)(dlt + rowb);
-                const f32x4 d_hi = *(const f32x4*)(dlt + rowb + 8);
-                bf16x8 pb, dsb;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int ei = (t & 1) * 8 + e;
-                    const float l2 = e < 4 ? l_lo[e] : l_hi[e - 4];
-                    const float dl = e < 4 ? d_lo[e] : d_hi[e - 4];
-                    const float pe = fast_exp2(__builtin_fmaf(s[rb][ei], c, -l2));
-                    pb[e] = (__bf16)pe;
-                    dsb[e] = (__bf16)(pe * (dp[rb][ei] - dl));
-                }
-#pragma unroll
-                for (int db = 0; db < DB; db++) {
-                    const unsigned short* gp = Gs + (t * 16 + key_l) * Q::QP + db * 32 + col_l;
-                    const unsigned short* qp = Qs + (t * 16 + key_l) * Q::QP + db * 32 + col_l;
-                    const i16x4 glo = lds_read_tr16(gp), ghi = lds_read_tr16(gp + 8 * Q::QP);
-                    const i16x4 qlo = lds_read_tr16(qp), qhi = lds_read_tr16(qp + 8 * Q::QP);
-                    const bf16x8 ga = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    const bf16x8 qa = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pb, dvacc[db], 0, 0, 0);
-                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsb, dkacc[db], 0, 0, 0);
-                }
-                // this step's transposed reads, then its MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 4 * DB, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * DB, 0);
+            for (int db = 0; db < DB; db++) {
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[t & 1].g[db], pb[t],
+                                                                    dvacc[db], 0, 0, 0);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[t & 1].q[db], dsb[t],
+                                                                    dkacc[db], 0, 0, 0);
             }
         }
-        if (has_next) store_step(stage ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // stage (st + 2) % NS held tile st - 1, which every wave finished before
+        // the previous barrier
+        store_step(stage_store);
         __syncthreads();
+    };
+    for (int st = 0; st < n_steps; st += 2) {
+        step(st, std::integral_constant<int, 0>{});
+        if (st + 1 < n_steps) step(st + 1, std::integral_constant<int, 1>{});
     }
 
     if (!key_ok) return;
@@ -458,8 +558,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
                 k4[e] = (__bf16)(dkacc[db][jq * 4 + e] * bp.scale);
                 v4[e] = (__bf16)dvacc[db][jq * 4 + e];
             }
-            *(bf16x4*)(dkp + db * 32 + jq * 8 + half * 4) = k4;
-            *(bf16x4*)(dvp + db * 32 + jq * 8 + half * 4) = v4;
+            *(bf16x4*)(dkp + acc_dim(db, jq, half)) = k4;
+            *(bf16x4*)(dvp + acc_dim(db, jq, half)) = v4;
         }
 }
 
