@@ -239,6 +239,19 @@ def _report(name, ms, ms_min, flop, bytes_, extra=None):
     return r
 
 
+def encoder_pairs(c) -> int:
+    """Exact attended pairs per (b, h) of the bidirectional encoder with global
+    tokens: the band, the global keys outside it, and whole rows for the
+    global queries."""
+    N = c["N"]
+    G = np.array(sorted(set(c["global_idx"])))
+    i = np.arange(N)
+    band = np.minimum(i, c["win_left"]) + np.minimum(N - 1 - i, c["win_right"]) + 1
+    far = ((G[None, :] < i[:, None] - c["win_left"]) |
+           (G[None, :] > i[:, None] + c["win_right"])).sum(1)
+    return int(np.where(np.isin(i, G), N, band + far).sum())
+
+
 def bench_other_workloads():
     """The bidirectional encoder with global tokens, the four layers of the
     dilated stack and one chunk of a chunked prefill, each timed per call and
@@ -253,11 +266,7 @@ def bench_other_workloads():
     B, H, N, D = c["B"], c["Hq"], c["N"], c["D"]
     q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], B, H, H, N, D, c["dtype"]))
     G = np.array(sorted(set(c["global_idx"])))
-    i = np.arange(N)
-    band = np.minimum(i, c["win_left"]) + np.minimum(N - 1 - i, c["win_right"]) + 1
-    far = ((G[None, :] < i[:, None] - c["win_left"]) |
-           (G[None, :] > i[:, None] + c["win_right"])).sum(1)
-    pairs = np.where(np.isin(i, G), N, band + far).sum()
+    pairs = encoder_pairs(c)
     flop = 4.0 * B * H * D * float(pairs)
     bytes_ = 4.0 * B * N * H * D * 2 + 4.0 * B * H * N
     ws = torch.empty(binding.fwd_workspace_size(B, H, N, D, len(G)), dtype=torch.uint8,
@@ -315,7 +324,33 @@ def bench_other_workloads():
     del q, k, v, kc, vc, kc2, vc2, out, lse
     res.extend(bench_decode_variants())
     res.append(bench_bwd())
+    res.append(bench_bwd_globals())
     return res
+
+
+def bench_bwd_globals():
+    """Backward of the bidirectional encoder with 16 global tokens: the band
+    passes plus the passes over the global tokens' pairs outside the band."""
+    import torch
+    from sliding_window_attention_tiled_amd import binding, configs
+    from sliding_window_attention_tiled_amd.inputs import fwd_inputs
+
+    c = configs.FWD["bidir_encoder_globals"]
+    B, H, N, D = c["B"], c["Hq"], c["N"], c["D"]
+    G = c["global_idx"]
+    q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], B, H, H, N, D, c["dtype"]))
+    g = to_dev(fwd_inputs(c["seed"] + 100, B, H, H, N, D, c["dtype"])[0])
+    kw = dict(win_left=c["win_left"], win_right=c["win_right"], global_idx=G)
+    out, lse = binding.fwd(q, k, v, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(binding.bwd_workspace_size(B, H, H, N, D, len(G)), dtype=torch.uint8,
+                     device="cuda")
+    ms, mn = _time_calls(lambda: binding.bwd(q, k, v, out, lse, g, dq=dq, dk=dk, dv=dv,
+                                             workspace=ws, **kw))
+    flop = 10.0 * B * H * D * float(encoder_pairs(c))
+    bytes_ = (4.0 * B * N * H * D + 4.0 * B * N * H * D) * 2 + 8.0 * B * H * N
+    return _report("bwd_bidir_encoder_globals", ms, mn, flop, bytes_,
+                   {"flop_per_pair": "10*D algorithmic"})
 
 
 def bench_bwd():
@@ -334,7 +369,7 @@ def bench_bwd():
     g = to_dev(fwd_inputs(c["seed"] + 100, B, Hq, Hkv, N, D, c["dtype"])[0])
     out, lse = binding.fwd(q, k, v, win_left=c["win_left"])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(binding.bwd_workspace_size(B, Hq, N, D), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(binding.bwd_workspace_size(B, Hq, Hkv, N, D), dtype=torch.uint8, device="cuda")
     ms, mn = _time_calls(lambda: binding.bwd(q, k, v, out, lse, g, win_left=c["win_left"],
                                              dq=dq, dk=dk, dv=dv, workspace=ws))
     pairs = exact_pairs_causal(N, W)

@@ -333,15 +333,20 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
  *   dk, dv               device, [B, N, Hkv, D] of `dtype` (written; keys no
  *                        query attends get 0)
  *   win_left, win_right, dilation, scale   as for swa_fwd
- *   global_idx, n_global must describe no global token (n_global == 0):
- *                        the backward of global tokens is not provided
+ *   global_idx, n_global as for swa_fwd (host array).  Global rows take the
+ *                        terms of every key they attend, every row the terms
+ *                        of the global keys it attends (aiqz.cc "Sliding
+ *                        window attention: Mistral", section "global attention
+ *                        tokens").  The pairs outside the band are summed in
+ *                        float32 and added to the band's dq, dk, dv (one more
+ *                        rounding of those rows in bf16).
  *   workspace            device scratch of swa_bwd_workspace_size() bytes
- *                        (per-row dout . out); two calls in flight at once
- *                        must not share it
+ *                        (per-row dout . out; with global tokens also float32
+ *                        accumulators of their rows and keys); two calls in
+ *                        flight at once must not share it
  *
  * Errors: as swa_fwd (with lse, dout, dq, dk, dv required), plus
- * SWA_ERR_UNSUPPORTED when n_global > 0 and SWA_ERR_WORKSPACE for a missing
- * or short workspace.
+ * SWA_ERR_WORKSPACE for a missing or short workspace.
  */
 int swa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
             const void* dout, void* dq, void* dk, void* dv,
@@ -351,8 +356,9 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             float scale, int dtype,
             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace swa_bwd needs (0 on bad sizes). */
-size_t swa_bwd_workspace_size(int B, int Hq, int N, int D);
+/* Bytes of device workspace swa_bwd needs for n_global global tokens (the
+ * count passed to swa_bwd, duplicates included, is enough); 0 on bad sizes. */
+size_t swa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int n_global);
 
 /* A static, human-readable description of a status code. */
 const char* swa_status_string(int status);

@@ -64,7 +64,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, I, F, I, P,
                             SZ, P]
     lib.swa_bwd.restype = I
-    lib.swa_bwd_workspace_size.argtypes = [I, I, I, I]
+    lib.swa_bwd_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.swa_bwd_workspace_size.restype = SZ
     lib.swa_decode_workspace_size.argtypes = [I, I, I, I]
     lib.swa_decode_workspace_size.restype = SZ
@@ -359,17 +359,17 @@ def decode_paged(q: torch.Tensor, kpool: torch.Tensor, vpool: torch.Tensor,
     return (out, lse) if return_lse else out
 
 
-def bwd_workspace_size(B: int, Hq: int, N: int, D: int) -> int:
-    return int(load_library().swa_bwd_workspace_size(B, Hq, N, D))
+def bwd_workspace_size(B: int, Hq: int, Hkv: int, N: int, D: int, n_global: int = 0) -> int:
+    return int(load_library().swa_bwd_workspace_size(B, Hq, Hkv, N, D, n_global))
 
 
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, *, win_left: int, win_right: int = 0, dilation: int = 1,
-        scale: float | None = None, dq: torch.Tensor | None = None,
+        global_idx=None, scale: float | None = None, dq: torch.Tensor | None = None,
         dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
         workspace: torch.Tensor | None = None):
     """Gradients (dq, dk, dv) of fwd for the upstream gradient dout; out and lse
-    from fwd with the same arguments."""
+    from fwd with the same arguments (global_idx included)."""
     lib = load_library()
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -386,12 +386,16 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, ls
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = bwd_workspace_size(B, Hq, N, D)
+    g, ng = None, 0
+    if global_idx is not None and len(global_idx):
+        g = (ctypes.c_int32 * len(global_idx))(*[int(x) for x in global_idx])
+        ng = len(global_idx)
+    need = bwd_workspace_size(B, Hq, Hkv, N, D, ng)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib.swa_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
                      _dev(lse, "lse"), _dev(dout, "dout"), _dev(dq, "dq"), _dev(dk, "dk"),
-                     _dev(dv, "dv"), B, Hq, Hkv, N, D, win_left, win_right, dilation, None, 0,
+                     _dev(dv, "dv"), B, Hq, Hkv, N, D, win_left, win_right, dilation, g, ng,
                      float(scale), _dtype_code(q), _dev(workspace, "workspace"),
                      workspace.numel() * workspace.element_size(), _stream(q))
     _check(st, "swa_bwd")

@@ -31,6 +31,17 @@ void global_chunks(int N, int* chunk, int* nchunks) {
     *nchunks = (int)cdiv(N, ck);
 }
 
+// The global positions sorted and deduplicated; SWA_ERR_ARG for a position
+// outside [0, N), SWA_ERR_UNSUPPORTED for more than SWA_MAX_GLOBAL of them.
+int normalize_globals(const int32_t* global_idx, int n_global, int N, std::vector<int32_t>& g) {
+    g.assign(global_idx, global_idx + n_global);
+    for (int32_t x : g)
+        if (x < 0 || x >= N) return SWA_ERR_ARG;
+    std::sort(g.begin(), g.end());
+    g.erase(std::unique(g.begin(), g.end()), g.end());
+    return (int)g.size() > SWA_MAX_GLOBAL ? SWA_ERR_UNSUPPORTED : SWA_OK;
+}
+
 // Splits of a decode ring: enough workgroups to cover the GPU several times
 // over, each split a multiple of 128 slots.
 void decode_splits(int B, int Hq, int W, int* splits, int* per_split) {
@@ -128,12 +139,8 @@ int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
 
     std::vector<int32_t> g;
     if (n_global > 0) {
-        g.assign(global_idx, global_idx + n_global);
-        for (int32_t x : g)
-            if (x < 0 || x >= N) return SWA_ERR_ARG;
-        std::sort(g.begin(), g.end());
-        g.erase(std::unique(g.begin(), g.end()), g.end());
-        if ((int)g.size() > SWA_MAX_GLOBAL) return SWA_ERR_UNSUPPORTED;
+        const int st = normalize_globals(global_idx, n_global, N, g);
+        if (st != SWA_OK) return st;
         if (!workspace || workspace_bytes < swa_fwd_workspace_size(B, Hq, N, D, (int)g.size()))
             return SWA_ERR_WORKSPACE;
     }
@@ -368,9 +375,25 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
     return combine_decode(p, out, lse, D, dtype, stream);
 }
 
-size_t swa_bwd_workspace_size(int B, int Hq, int N, int D) {
-    if (B <= 0 || Hq <= 0 || N <= 0 || N > kMaxN || !supported_d(D)) return 0;
-    return ((size_t)B * Hq * N * sizeof(float) + 255) / 256 * 256;
+// Workspace of swa_bwd: per-row dout . out, then (global tokens only) the
+// float32 accumulators of the global rows' dq and the global keys' dk, dv.
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t bwd_delta_bytes(int B, int Hq, int N) {
+    return align256((size_t)B * Hq * N * sizeof(float));
+}
+static size_t bwd_dq_acc_bytes(int B, int Hq, int ng, int D) {
+    return align256((size_t)B * Hq * ng * D * sizeof(float));
+}
+
+size_t swa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int n_global) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || N > kMaxN || !supported_d(D)) return 0;
+    if (n_global < 0) return 0;
+    const int ng = std::min(n_global, std::min(N, SWA_MAX_GLOBAL));
+    size_t bytes = bwd_delta_bytes(B, Hq, N);
+    if (ng > 0)
+        bytes += bwd_dq_acc_bytes(B, Hq, ng, D) +
+                 align256((size_t)B * Hkv * ng * 2 * D * sizeof(float));
+    return bytes;
 }
 
 int swa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -384,8 +407,13 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
     if (win_left < 0 || win_right < 0 || dilation < 1) return SWA_ERR_ARG;
     if (n_global < 0 || (n_global > 0 && !global_idx)) return SWA_ERR_ARG;
     if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
-    if (n_global > 0) return SWA_ERR_UNSUPPORTED;  // global tokens: forward only
-    if (!workspace || workspace_bytes < swa_bwd_workspace_size(B, Hq, N, D))
+    std::vector<int32_t> g;
+    if (n_global > 0) {
+        const int st = normalize_globals(global_idx, n_global, N, g);
+        if (st != SWA_OK) return st;
+    }
+    const int ng = (int)g.size();
+    if (!workspace || workspace_bytes < swa_bwd_workspace_size(B, Hq, Hkv, N, D, ng))
         return SWA_ERR_WORKSPACE;
 
     swa::BwdParams bp;
@@ -425,9 +453,53 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
     bp.ktiles_per_slab = (int)per_slab;
     bp.k_blocks = (int)kblocks;
 
+    // the global tokens' pairs outside the band: workgroup splits
+    swa::GlobalBwdParams gb;
+    std::memset(&gb, 0, sizeof gb);
+    if (ng > 0) {
+        gb.q = q;
+        gb.k = k;
+        gb.v = v;
+        gb.dout = dout;
+        gb.lse = lse;
+        gb.delta = bp.delta;
+        gb.dq = dq;
+        gb.dk = dk;
+        gb.dv = dv;
+        char* ws = (char*)workspace + bwd_delta_bytes(B, Hq, N);
+        gb.dq_acc = (float*)ws;
+        gb.dkv_acc = (float*)(ws + bwd_dq_acc_bytes(B, Hq, ng, D));
+        gb.B = B;
+        gb.Hq = Hq;
+        gb.Hkv = Hkv;
+        gb.N = N;
+        gb.group = p.group;
+        gb.wl = p.wl;
+        gb.wr = p.wr;
+        gb.dil = dilation;
+        gb.causal = p.causal;
+        gb.scale = scale;
+        gb.scale_log2 = p.scale_log2;
+        gb.n_global = ng;
+        for (int i = 0; i < ng; i++) gb.gpos[i] = g[i];
+        gb.row_tiles = gb.key_tiles = (int)cdiv(ng, 64);
+        // splits of the N keys (rows) so that each pass has about 2048 workgroups
+        const int64_t nkc = std::min<int64_t>(
+            cdiv(N, 256), std::max<int64_t>(1, cdiv(2048, (int64_t)B * Hq * gb.row_tiles)));
+        gb.key_chunk = (int)(cdiv(cdiv(N, nkc), 32) * 32);
+        gb.n_key_chunks = (int)cdiv(N, gb.key_chunk);
+        const int64_t nrc = std::min<int64_t>(
+            cdiv(N, 256), std::max<int64_t>(1, cdiv(2048, (int64_t)B * Hkv * gb.key_tiles)));
+        gb.row_chunk = (int)(cdiv(cdiv(N, nrc), 32) * 32);
+        gb.n_row_chunks = (int)cdiv(N, gb.row_chunk);
+        gb.n_row_tiles_all = gb.n_key_tiles_all = (int)cdiv(N, 64);
+        if ((int64_t)B * Hq * gb.n_row_tiles_all > INT32_MAX) return SWA_ERR_ARG;
+    }
+
     if (swa::launch_bwd_delta(bp, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
     hipError_t e = dtype == SWA_BF16 ? swa::launch_bwd_bf16(bp, D, stream)
                                      : swa::launch_bwd_f32(bp, D, stream);
+    if (e == hipSuccess && ng > 0) e = swa::launch_bwd_global(gb, D, dtype, stream);
     return e == hipSuccess ? SWA_OK : SWA_ERR_HIP;
 }
 

@@ -78,6 +78,33 @@ struct BwdParams {
     int k_blocks;                   // grid of the key-major pass
 };
 
+// The backward's pairs outside the band that global tokens add (global rows
+// with every key, every row with the global keys); see bwd_global.hip.
+struct GlobalBwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;    // [B][Hq][N]
+    const float* delta;  // [B][Hq][N]
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dq_acc;       // [B][Hq][n_global][D] float32, cleared by the launch
+    float* dkv_acc;      // [B][Hkv][n_global][2][D] float32, cleared by the launch
+    int B, Hq, Hkv, N, group;
+    int wl, wr, dil, causal;
+    float scale, scale_log2;
+    int n_global;
+    int row_tiles;        // 64-row tiles of the global rows
+    int key_chunk, n_key_chunks;   // key split of the global-row dq pass
+    int key_tiles;        // 64-key tiles of the global keys
+    int row_chunk, n_row_chunks;   // row split of the global-key dk/dv pass
+    int n_row_tiles_all;  // 64-row tiles of all N rows
+    int n_key_tiles_all;  // 64-key tiles of all N keys
+    int32_t gpos[SWA_MAX_GLOBAL];  // sorted, unique
+};
+
 struct DecodeParams {
     const void* q;
     const void* kcache;
@@ -133,6 +160,7 @@ int bwd_f32_dkdv_keys();
 hipError_t launch_bwd_delta(const BwdParams& p, int D, int dtype, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int D, hipStream_t s);
+hipError_t launch_bwd_global(const GlobalBwdParams& g, int D, int dtype, hipStream_t s);
 hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn,
                             int32_t* head, int32_t* len, int B, int Hkv, int W, int D,
                             int elem_bytes, hipStream_t s);

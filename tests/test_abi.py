@@ -246,8 +246,12 @@ def test_bwd_validation(lib):
     f = lib.swa_bwd
     names = ["q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "B", "Hq", "Hkv", "N", "D",
              "wl", "wr", "dil", "g", "ng", "scale", "dtype", "ws", "wsb", "stream"]
-    need = lib.swa_bwd_workspace_size(1, 4, 128, 128)
-    assert need >= 4 * 128 * 4 and lib.swa_bwd_workspace_size(1, 4, 128, 96) == 0
+    need = lib.swa_bwd_workspace_size(1, 4, 2, 128, 128, 0)
+    assert need >= 4 * 128 * 4 and lib.swa_bwd_workspace_size(1, 4, 2, 128, 96, 0) == 0
+    assert lib.swa_bwd_workspace_size(1, 4, 2, 128, 128, -1) == 0
+    # global tokens add float32 accumulators of their rows (dq) and keys (dk, dv)
+    need_g = lib.swa_bwd_workspace_size(1, 4, 2, 128, 128, 2)
+    assert need_g >= need + (4 * 2 * 128 + 2 * 2 * 2 * 128) * 4
     base = [P, P, P, P, P, P, P, P, P, 1, 4, 2, 128, 128, 7, 0, 1, None, 0, 0.1, 1, P, need,
             None]
 
@@ -261,6 +265,10 @@ def test_bwd_validation(lib):
     assert call(Hq=6, Hkv=4) == ARG and call(wl=-1) == ARG and call(dil=0) == ARG
     assert call(N=(1 << 28) + 1) == ARG
     assert call(D=80) == UNSUP and call(dtype=5) == UNSUP
-    g = (ctypes.c_int32 * 2)(0, 5)
-    assert call(g=g, ng=2) == UNSUP                     # no backward of global tokens
+    # global tokens: checked (and the workspace sized) before any launch
+    assert call(g=(ctypes.c_int32 * 2)(0, 128), ng=2) == ARG        # position >= N
+    assert call(g=None, ng=2) == ARG and call(ng=-1) == ARG
+    many = (ctypes.c_int32 * 300)(*range(300))
+    assert call(N=1024, g=many, ng=300) == UNSUP                     # > 256 distinct
+    assert call(g=(ctypes.c_int32 * 2)(0, 5), ng=2) == WS            # no room for them
     assert call(ws=None) == WS and call(wsb=need - 1) == WS

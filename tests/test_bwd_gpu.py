@@ -31,11 +31,12 @@ SMALL = [
 ]
 
 
-def _run(q, k, v, g, dt, wl, wr, dil, scale):
+def _run(q, k, v, g, dt, wl, wr, dil, scale, G=None):
     qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
-    out, lse = binding.fwd(qd, kd, vd, win_left=wl, win_right=wr, dilation=dil, scale=scale)
+    out, lse = binding.fwd(qd, kd, vd, win_left=wl, win_right=wr, dilation=dil, scale=scale,
+                           global_idx=G)
     dq, dk, dv = binding.bwd(qd, kd, vd, out, lse, gd, win_left=wl, win_right=wr,
-                             dilation=dil, scale=scale)
+                             dilation=dil, global_idx=G, scale=scale)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -68,6 +69,57 @@ def test_bwd_small(case):
     _check_grad(to_host_f64(dq), rq, dt, f"{name} dq")
     _check_grad(to_host_f64(dk), rk, dt, f"{name} dk")
     _check_grad(to_host_f64(dv), rv, dt, f"{name} dv")
+
+
+GLOBAL_CASES = [
+    # name, B, Hq, Hkv, N, D, dtype, wl, wr, dil, scale, global positions
+    ("g_bidir_gqa4_d128", 1, 8, 2, 300, 128, "bf16", 40, 40, 1, None, [0, 7, 150, 299]),
+    ("g_causal_mha_d64", 2, 4, 4, 257, 64, "bf16", 30, 0, 1, None, [0, 100, 256]),
+    ("g_dilated3_gqa2", 1, 4, 2, 400, 128, "bf16", 20, 0, 3, None, [3, 5, 200, 201, 399]),
+    ("g_many_bidir", 1, 2, 1, 700, 64, "bf16", 16, 16, 1, None, list(range(0, 700, 7))),
+    ("g_f32_dilated_bidir", 1, 2, 2, 150, 64, "f32", 7, 5, 2, 0.3, [0, 1, 2, 75, 149]),
+    ("g_f32_causal_d128", 1, 4, 1, 333, 128, "f32", 50, 0, 1, None, [10, 20, 330, 20]),
+]
+
+
+@pytest.mark.parametrize("case", GLOBAL_CASES, ids=[c[0] for c in GLOBAL_CASES])
+def test_bwd_global_tokens_small(case):
+    """Global rows attend every key and every row attends the global keys: the
+    backward's pairs outside the band, every element against the oracle."""
+    name, B, Hq, Hkv, N, D, dt, wl, wr, dil, scale, G = case
+    q, k, v = fwd_inputs(95, B, Hq, Hkv, N, D, dt)
+    g = fwd_inputs(96, B, Hq, Hkv, N, D, dt)[0]
+    log(f"[bwd] {name}")
+    dq, dk, dv = _run(q, k, v, g, dt, wl, wr, dil, scale, G)
+    rq, rk, rv = oracle.bwd(q, k, v, g, win_left=wl, win_right=wr, dilation=dil,
+                            global_idx=G, scale=scale)
+    _check_grad(to_host_f64(dq), rq, dt, f"{name} dq")
+    _check_grad(to_host_f64(dk), rk, dt, f"{name} dk")
+    _check_grad(to_host_f64(dv), rv, dt, f"{name} dv")
+
+
+def test_bwd_full_size_global_tokens_sampled():
+    """The bidirectional encoder layer with 16 global tokens at full size:
+    sampled dq rows and dk/dv keys, global ones included."""
+    c = configs.FWD["bidir_encoder_globals"]
+    B, Hq, Hkv, N, D, dt = c["B"], c["Hq"], c["Hkv"], c["N"], c["D"], c["dtype"]
+    G = c["global_idx"]
+    wl, wr = c["win_left"], c["win_right"]
+    q, k, v = fwd_inputs(c["seed"], B, Hq, Hkv, N, D, dt)
+    g = fwd_inputs(c["seed"] + 100, B, Hq, Hkv, N, D, dt)[0]
+    log("[bwd] bidirectional encoder with globals, full size")
+    dq, dk, dv = _run(q, k, v, g, dt, wl, wr, 1, None, G)
+    rng = np.random.Generator(np.random.PCG64(97))
+    picks = [0, 512, 4096, 8192 - 512, 1, 511, 513, N - 1] + rng.integers(0, N, 4).tolist()
+    rows = np.array([[int(rng.integers(0, B)), int(rng.integers(0, Hq)), int(i)] for i in picks])
+    ref = oracle.bwd_dq_rows(q, k, v, g, rows, win_left=wl, win_right=wr, global_idx=G)
+    got = to_host_f64(dq)
+    _check_grad(np.stack([got[b, i, h] for b, h, i in rows]), ref, dt, "globals sampled dq")
+    sel = np.array([[int(rng.integers(0, B)), int(rng.integers(0, Hkv)), int(j)] for j in picks])
+    rk, rv = oracle.bwd_dkv_keys(q, k, v, g, sel, win_left=wl, win_right=wr, global_idx=G)
+    gk, gv = to_host_f64(dk), to_host_f64(dv)
+    _check_grad(np.stack([gk[b, j, h] for b, h, j in sel]), rk, dt, "globals sampled dk")
+    _check_grad(np.stack([gv[b, j, h] for b, h, j in sel]), rv, dt, "globals sampled dv")
 
 
 def test_bwd_full_size_mistral_sampled():
