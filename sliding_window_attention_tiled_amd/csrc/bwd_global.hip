@@ -11,8 +11,11 @@
 //   E_col = {(i, g): i not global, g global, g not in band(i)}  (global keys)
 // each with j <= i when causal.  They are few (at most 256 rows or keys per
 // head), so these kernels work on the vector ALUs in float32, in the layout of
-// the float32 backward: 64 rows (or keys) per workgroup, four lanes each, and
-// tiles of 32 partners (keys, or query rows) staged in LDS.  Same chain rule as
+// the float32 backward: rows (or keys) of a workgroup spread over lanes, with
+// tiles of 32 partners (keys, or query rows) staged in LDS.  The passes over all
+// N rows or keys take 64 per workgroup, four lanes each; the passes whose items
+// are the global tokens take kGlobalBwdItems per workgroup, sixteen lanes each,
+// so that a few tokens still fill the workgroup.  Same chain rule as
 // the band passes: dS = P (dP - delta), dq = scale sum dS k, dk = scale sum dS q,
 // dv = sum P dout.
 //   rows_dq    dq of global rows over E_row, per key chunk, float32 atomics
@@ -30,8 +33,8 @@ namespace {
 
 constexpr float kLog2eG = 1.4426950408889634f;
 constexpr int TK = 32;     // partners per LDS tile
-constexpr int ITEMS = 64;  // rows or keys per workgroup
-constexpr int NT = 256;    // four lanes per item
+constexpr int ITEMS = 64;  // rows or keys per workgroup of the all-N passes
+constexpr int NT = 256;    // threads per workgroup
 
 template <typename T>
 __device__ __forceinline__ f32x4 ld4(const T* p);
@@ -85,21 +88,26 @@ __device__ __forceinline__ void copy_gpos(const GlobalBwdParams& g, int* gp) {
     for (int i = threadIdx.x; i < g.n_global; i += NT) gp[i] = g.gpos[i];
 }
 
-// sum over the four lanes of an item
-__device__ __forceinline__ float quad_sum(float x) {
-    x += __shfl_xor(x, 1);
-    return x + __shfl_xor(x, 2);
+// sum over the LANES consecutive lanes of an item
+template <int LANES>
+__device__ __forceinline__ float item_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < LANES; m <<= 1) x += __shfl_xor(x, m);
+    return x;
 }
+__device__ __forceinline__ float quad_sum(float x) { return item_sum<4>(x); }
 
 // ---- rows_dq: dq of global rows over E_row ------------------------------------
-// grid: (b, hq, 64-row tile of the global rows, key chunk)
+// grid: (b, hq, tile of kGlobalBwdItems global rows, key chunk).  Few rows per
+// workgroup, so each row takes NT / kGlobalBwdItems lanes.
 template <int D, typename T>
 __global__ __launch_bounds__(NT) void rows_dq_kernel(const GlobalBwdParams g) {
-    constexpr int DQ = D / 4;
+    constexpr int LANES = NT / kGlobalBwdItems;
+    constexpr int DQ = D / LANES;
     constexpr int PITCH = D + 4;
     __shared__ __attribute__((aligned(16))) float ks[TK * PITCH];
     __shared__ __attribute__((aligned(16))) float vs[TK * PITCH];
-    const int tid = threadIdx.x, part = tid & 3;
+    const int tid = threadIdx.x, part = tid % LANES;
     int L = blockIdx.x;
     const int chunk = L % g.n_key_chunks;
     L /= g.n_key_chunks;
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(NT) void rows_dq_kernel(const GlobalBwdParams g) {
     const int hq = L % g.Hq;
     const int b = L / g.Hq;
     const int kvh = hq / g.group;
-    const int gi = rt * ITEMS + (tid >> 2);
+    const int gi = rt * kGlobalBwdItems + tid / LANES;
     const bool row_ok = gi < g.n_global;
     const int i = row_ok ? g.gpos[gi] : 0;
 
@@ -150,8 +158,8 @@ __global__ __launch_bounds__(NT) void rows_dq_kernel(const GlobalBwdParams g) {
                 sd = __builtin_fmaf(q[d], ks[kk * PITCH + part * DQ + d], sd);
                 pd = __builtin_fmaf(dq[d], vs[kk * PITCH + part * DQ + d], pd);
             }
-            sd = quad_sum(sd);
-            pd = quad_sum(pd);
+            sd = item_sum<LANES>(sd);
+            pd = item_sum<LANES>(pd);
             const int j = t0 + kk;
             const bool ok = row_ok && j < j1 && extra_pair(g, i, j);
             const float pe = ok ? fast_exp2(sd * g.scale_log2 - lse2) : 0.f;
@@ -168,16 +176,18 @@ __global__ __launch_bounds__(NT) void rows_dq_kernel(const GlobalBwdParams g) {
 }
 
 // ---- cols_dkdv: dk, dv of global keys over E_col -----------------------------
-// grid: (b, kv head, 64-key tile of the global keys, row chunk)
+// grid: (b, kv head, tile of kGlobalBwdItems global keys, row chunk); each key
+// takes NT / kGlobalBwdItems lanes
 template <int D, typename T>
 __global__ __launch_bounds__(NT) void cols_dkdv_kernel(const GlobalBwdParams g) {
-    constexpr int DQ = D / 4;
+    constexpr int LANES = NT / kGlobalBwdItems;
+    constexpr int DQ = D / LANES;
     constexpr int PITCH = D + 4;
     __shared__ __attribute__((aligned(16))) float qs[TK * PITCH];
     __shared__ __attribute__((aligned(16))) float gs[TK * PITCH];
     __shared__ float rl[3 * TK];   // lse2, delta, row taken (1) or not (0)
     __shared__ int gp[SWA_MAX_GLOBAL];
-    const int tid = threadIdx.x, part = tid & 3;
+    const int tid = threadIdx.x, part = tid % LANES;
     int L = blockIdx.x;
     const int chunk = L % g.n_row_chunks;
     L /= g.n_row_chunks;
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(NT) void cols_dkdv_kernel(const GlobalBwdParams g) 
     L /= g.key_tiles;
     const int kvh = L % g.Hkv;
     const int b = L / g.Hkv;
-    const int gk = kt * ITEMS + (tid >> 2);
+    const int gk = kt * kGlobalBwdItems + tid / LANES;
     const bool key_ok = gk < g.n_global;
     const int j = key_ok ? g.gpos[gk] : 0;
     copy_gpos(g, gp);
@@ -234,8 +244,8 @@ __global__ __launch_bounds__(NT) void cols_dkdv_kernel(const GlobalBwdParams g) 
                     sd = __builtin_fmaf(kx[d], qs[ri * PITCH + part * DQ + d], sd);
                     pd = __builtin_fmaf(vx[d], gs[ri * PITCH + part * DQ + d], pd);
                 }
-                sd = quad_sum(sd);
-                pd = quad_sum(pd);
+                sd = item_sum<LANES>(sd);
+                pd = item_sum<LANES>(pd);
                 const int i = r0 + ri;
                 const bool ok = key_ok && rl[2 * TK + ri] != 0.f && extra_pair(g, i, j);
                 const float pe = ok ? fast_exp2(sd * g.scale_log2 - rl[ri]) : 0.f;

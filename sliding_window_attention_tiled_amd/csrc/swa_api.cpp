@@ -482,7 +482,7 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         gb.scale_log2 = p.scale_log2;
         gb.n_global = ng;
         for (int i = 0; i < ng; i++) gb.gpos[i] = g[i];
-        gb.row_tiles = gb.key_tiles = (int)cdiv(ng, 64);
+        gb.row_tiles = gb.key_tiles = (int)cdiv(ng, swa::kGlobalBwdItems);
         // splits of the N keys (rows) so that each pass has about 2048 workgroups
         const int64_t nkc = std::min<int64_t>(
             cdiv(N, 256), std::max<int64_t>(1, cdiv(2048, (int64_t)B * Hq * gb.row_tiles)));

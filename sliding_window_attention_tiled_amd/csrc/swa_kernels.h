@@ -80,6 +80,8 @@ struct BwdParams {
 
 // The backward's pairs outside the band that global tokens add (global rows
 // with every key, every row with the global keys); see bwd_global.hip.
+// Global rows (keys) per workgroup of the passes whose items are global tokens.
+constexpr int kGlobalBwdItems = 16;
 struct GlobalBwdParams {
     const void* q;
     const void* k;
@@ -96,9 +98,9 @@ struct GlobalBwdParams {
     int wl, wr, dil, causal;
     float scale, scale_log2;
     int n_global;
-    int row_tiles;        // 64-row tiles of the global rows
+    int row_tiles;        // tiles of kGlobalBwdItems global rows
     int key_chunk, n_key_chunks;   // key split of the global-row dq pass
-    int key_tiles;        // 64-key tiles of the global keys
+    int key_tiles;        // tiles of kGlobalBwdItems global keys
     int row_chunk, n_row_chunks;   // row split of the global-key dk/dv pass
     int n_row_tiles_all;  // 64-row tiles of all N rows
     int n_key_tiles_all;  // 64-key tiles of all N keys
