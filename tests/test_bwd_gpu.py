@@ -79,6 +79,12 @@ GLOBAL_CASES = [
     ("g_many_bidir", 1, 2, 1, 700, 64, "bf16", 16, 16, 1, None, list(range(0, 700, 7))),
     ("g_f32_dilated_bidir", 1, 2, 2, 150, 64, "f32", 7, 5, 2, 0.3, [0, 1, 2, 75, 149]),
     ("g_f32_causal_d128", 1, 4, 1, 333, 128, "f32", 50, 0, 1, None, [10, 20, 330, 20]),
+    # every token global: no non-global rows, every pair outside the band is a global row's
+    ("g_all_global_f32", 1, 2, 1, 70, 64, "f32", 5, 0, 1, None, list(range(70))),
+    # window covering the sequence: the global tokens add no pair
+    ("g_window_ge_n", 1, 4, 2, 90, 128, "bf16", 200, 200, 1, None, [0, 45, 89]),
+    # three tokens, one global, causal
+    ("g_tiny_n", 1, 2, 2, 3, 64, "bf16", 1, 0, 1, None, [1]),
 ]
 
 
