@@ -209,7 +209,9 @@ int swa_fwd_cached(const void* q, const void* k, const void* v,
  *               (may be NULL)
  *   workspace   device scratch of at least swa_decode_workspace_size(B, Hq, W, D)
  *               bytes, owned by the caller; its contents on entry do not
- *               matter.  Two calls in flight at once must not share it.
+ *               matter.  It holds split partials; a bf16 launch whose rings
+ *               each take one slot range writes the rows directly and leaves
+ *               it untouched.  Two calls in flight at once must not share it.
  *
  * Errors: as swa_kv_append, plus SWA_ERR_ARG for Hq % Hkv != 0 and
  * SWA_ERR_WORKSPACE when the workspace is NULL or too small.
@@ -237,8 +239,10 @@ size_t swa_decode_workspace_size(int B, int Hq, int W, int D);
  *                 NULL when n_sink == 0.  Filling them: swa_kv_append_chunk on
  *                 a ring of n_sink slots starting at ring_head = cache_len = 0
  *                 puts token t of the chunk in slot t.
- *   n_sink        0 <= n_sink <= SWA_MAX_N; the sink entries form one extra
- *                 split per (b, kv head), so they should stay few next to W.
+ *   n_sink        0 <= n_sink <= SWA_MAX_N.  The bf16 kernel walks the sink
+ *                 entries in the first slot range of each (b, kv head), the
+ *                 fp32 kernel in a range of their own; either way they should
+ *                 stay few next to W.
  *   workspace     at least swa_decode_sinks_workspace_size(B, Hq, W, D, n_sink)
  *                 bytes.
  *   Everything else as for swa_decode (which is this call with n_sink == 0).

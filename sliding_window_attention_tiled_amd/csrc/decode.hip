@@ -11,7 +11,9 @@
 // for all heads.  Slots are visited in physical order (keys carry no position,
 // so order does not matter); a slot counts when its age
 // (ring_head - 1 - slot) mod W is below cache_len.  Each workgroup writes one
-// partial (acc, m, l) per head; the combine kernel merges the splits.
+// partial (acc, m, l) per head and the combine kernel merges the splits; with
+// a single split the workgroup holds the whole row and writes out and lse
+// itself.  Sink entries are walked by the first split of each (b, kv head).
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -160,8 +162,6 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     const bool head_ok = head_col < p.group;
     const int hq = kvh * p.group + head_col;
 
-    // the last split (when there are sinks) walks the sink entries, all valid
-    const bool sink_split = !PAGED && s >= p.ring_splits;
     const int W = p.W;
     const int ring_head = PAGED ? 0 : p.ring_head[b];
     // paged: live window positions pos0 .. pos0 + n_live - 1
@@ -169,16 +169,22 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     const int n_live = min(seq_n, W);
     const int pos0 = seq_n - n_live;
     const int cache_len = PAGED ? n_live : p.cache_len[b];
-    const bool full = sink_split || cache_len >= W;
-    const int src_slots = sink_split ? p.n_sink : W;
+    const bool full = cache_len >= W;
 
-    // slots of this wave
-    const int s_lo = sink_split ? 0 : s * p.slots_per_split;
-    const int s_hi = sink_split ? p.n_sink : min(W, s_lo + p.slots_per_split);
+    // ring slots of this wave
+    const int s_lo = s * p.slots_per_split;
+    const int s_hi = min(W, s_lo + p.slots_per_split);
     const int per_wave = (s_hi - s_lo + 3) / 4;
     const int w_lo = min(s_hi, s_lo + wave * per_wave);
     const int w_hi = min(s_hi, w_lo + per_wave);
     const int n_chunks = (w_hi - w_lo + CH - 1) / CH;
+    // the first split also walks the sink entries (all valid), a quarter per
+    // wave, as chunks n_chunks .. n_all - 1 of the wave
+    const int n_sk = (!PAGED && s == 0) ? p.n_sink : 0;
+    const int k_per = (n_sk + 3) / 4;
+    const int k_lo = min(n_sk, wave * k_per);
+    const int k_hi = min(n_sk, k_lo + k_per);
+    const int n_all = n_chunks + (k_hi - k_lo + CH - 1) / CH;
 
     // Q^T as the B operand: lane holds head column l16, dims ks*32 + grp*8 .. +7
     bf16x8 qreg[KS];
@@ -189,9 +195,11 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             qreg[k] = head_ok ? *(const bf16x8*)(qp + k * 32)
                               : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    const size_t slab = PAGED ? 0 : ((size_t)b * p.Hkv + kvh) * src_slots;
-    const __bf16* kbase = (const __bf16*)(sink_split ? p.ksink : p.kcache) + slab * D;
-    const __bf16* vbase = (const __bf16*)(sink_split ? p.vsink : p.vcache) + slab * D;
+    const size_t bk = (size_t)b * p.Hkv + kvh;
+    const __bf16* kbase = (const __bf16*)p.kcache + (PAGED ? 0 : bk * W * D);
+    const __bf16* vbase = (const __bf16*)p.vcache + (PAGED ? 0 : bk * W * D);
+    const __bf16* ksbase = n_sk > 0 ? (const __bf16*)p.ksink + bk * n_sk * D : kbase;
+    const __bf16* vsbase = n_sk > 0 ? (const __bf16*)p.vsink + bk * n_sk * D : vbase;
     unsigned short* Ks = smem + wave * C::WAVE_ELEMS;
     unsigned short* Vs = Ks + CH * C::PITCH;
 
@@ -229,26 +237,34 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     };
 
     u32x4 kr[C::PER_LANE], vr[C::PER_LANE];
+    // chunk ck of the wave: ring slots, or sink entries past the ring chunks
+    auto chunk_base = [&](int ck) -> int {
+        return !PAGED && ck >= n_chunks ? k_lo + (ck - n_chunks) * CH : w_lo + ck * CH;
+    };
+    auto chunk_end = [&](int ck) -> int { return !PAGED && ck >= n_chunks ? k_hi : w_hi; };
     auto load_chunk = [&](int ck) {
-        const int base = w_lo + ck * CH;
+        const bool sk = !PAGED && ck >= n_chunks;
+        const int base = chunk_base(ck), hi = chunk_end(ck);
+        const __bf16* kb = sk ? ksbase : kbase;
+        const __bf16* vb = sk ? vsbase : vbase;
 #pragma unroll
         for (int u = 0; u < C::PER_LANE; u++) {
             const int ci = lane + u * 64;
             const int key = ci / C::CPR, cc = ci % C::CPR;
             const int pg = PAGED && lane_pages ? lane_page(base + key) : 0;
-            if (base + key < w_hi && (!PAGED || base + key < n_live)) {
+            if (base + key < hi && (!PAGED || base + key < n_live)) {
                 const size_t off = (PAGED ? page_row(base + key, pg)
                                           : (size_t)(base + key) * D) + cc * 8;
-                kr[u] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
-                vr[u] = __builtin_nontemporal_load((const u32x4*)(vbase + off));
+                kr[u] = __builtin_nontemporal_load((const u32x4*)(kb + off));
+                vr[u] = __builtin_nontemporal_load((const u32x4*)(vb + off));
             } else {
                 kr[u] = u32x4{0u, 0u, 0u, 0u};
                 vr[u] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
-    if (n_chunks > 0) load_chunk(0);
-    for (int ck = 0; ck < n_chunks; ck++) {
+    if (n_all > 0) load_chunk(0);
+    for (int ck = 0; ck < n_all; ck++) {
         // stage the chunk in this wave's LDS area (natural [slot][d] layout)
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             *(u32x4*)(Vs + key * C::PITCH + cc * 8) = vr[u];
         }
         __builtin_amdgcn_wave_barrier();
-        if (ck + 1 < n_chunks) load_chunk(ck + 1);
+        if (ck + 1 < n_all) load_chunk(ck + 1);
 
         // S^T = K Q^T: two 16-slot blocks
         f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -271,16 +287,17 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
                 sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[k], sc[kb], 0, 0, 0);
             }
         // mask slots beyond the wave range or older than cache_len
-        const int base = w_lo + ck * CH;
+        const bool sk = !PAGED && ck >= n_chunks;
+        const int base = chunk_base(ck), hi = chunk_end(ck);
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int slot = base + kb * 16 + grp * 4 + e;
-                bool valid = slot < w_hi;
+                bool valid = slot < hi;
                 if (PAGED) {
                     valid = valid && slot < n_live;
-                } else if (!full) {
+                } else if (!full && !sk) {
                     int age = ring_head - 1 - slot;
                     if (age < 0) age += W;
                     valid = valid && age < cache_len;
@@ -355,11 +372,20 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             lsum += f * red_ml[(w * 16 + h) * 2 + 1];
         }
         const int hq2 = kvh * p.group + hb * 16 + h;
-        float* rec = p.partials + (((size_t)b * p.Hq + hq2) * p.splits + s) * (D + kPartialPad);
-        rec[d] = acc;
-        if (d == 0) {
-            rec[D] = M;
-            rec[D + 1] = lsum;
+        if (p.out != nullptr) {
+            // one split: this is the whole row, finished as the combine would
+            const size_t row = (size_t)b * p.Hq + hq2;
+            const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+            ((__bf16*)p.out)[row * D + d] = (__bf16)(acc * inv);
+            if (p.lse != nullptr && d == 0)
+                p.lse[row] = lsum > 0.f ? (M + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
+        } else {
+            float* rec = p.partials + (((size_t)b * p.Hq + hq2) * p.splits + s) * (D + kPartialPad);
+            rec[d] = acc;
+            if (d == 0) {
+                rec[D] = M;
+                rec[D + 1] = lsum;
+            }
         }
     }
 }

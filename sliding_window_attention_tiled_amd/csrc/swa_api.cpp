@@ -42,15 +42,34 @@ int normalize_globals(const int32_t* global_idx, int n_global, int N, std::vecto
     return (int)g.size() > SWA_MAX_GLOBAL ? SWA_ERR_UNSUPPORTED : SWA_OK;
 }
 
-// Splits of a decode ring: enough workgroups to cover the GPU several times
-// over, each split a multiple of 128 slots.
-void decode_splits(int B, int Hq, int W, int* splits, int* per_split) {
-    const int64_t rows = (int64_t)B * Hq;
-    int64_t sp = std::max<int64_t>(1, cdiv(8192, rows));
+// Splits of a decode ring, each a multiple of 128 slots.  The bf16 kernel runs
+// one 4-wave workgroup per (sequence, kv head, 16-head block, split) and two of
+// them are resident per CU at D = 128: about 512 workgroups fill the 256 CUs
+// once, and fewer, longer splits start and drain fewer workgroups and leave
+// fewer partials to merge (none with one split).  The f32 kernel runs one
+// wave per (sequence, query head, split) and aims at 8192 waves.
+constexpr int64_t kDecodeWorkgroups = 512;
+constexpr int64_t kDecodeWavesF32 = 8192;
+
+void decode_splits(int dtype, int B, int Hq, int Hkv, int W, int* splits, int* per_split) {
+    const int64_t units = dtype == SWA_BF16 ? (int64_t)B * Hkv * cdiv(Hq / Hkv, 16)
+                                            : (int64_t)B * Hq;
+    const int64_t target = dtype == SWA_BF16 ? kDecodeWorkgroups : kDecodeWavesF32;
+    int64_t sp = std::max<int64_t>(1, cdiv(target, units));
     sp = std::min<int64_t>(sp, std::max<int64_t>(1, W / 128));
     int64_t ps = cdiv(cdiv(W, sp), 128) * 128;
     *per_split = (int)ps;
     *splits = (int)cdiv(W, ps);
+}
+
+// Partials per row that a decode of these sizes can use, for either dtype and
+// any Hkv dividing Hq: the bf16 kernel makes the most splits at Hkv = 1 (the
+// fewest workgroup units), the f32 kernel adds one split for the sinks.
+int decode_max_splits(int B, int Hq, int W, int n_sink) {
+    int sb, sf, per;
+    decode_splits(SWA_BF16, B, Hq, 1, W, &sb, &per);
+    decode_splits(SWA_F32, B, Hq, Hq, W, &sf, &per);
+    return std::max(sb, sf + (n_sink > 0 ? 1 : 0));
 }
 
 // Band work decomposition of a forward launch (p.B, Hkv, group, N, dil set).
@@ -91,6 +110,24 @@ int combine_decode(const DecodeParams& p, void* out, float* lse, int D, int dtyp
     c.B = p.B;
     c.Hq = p.Hq;
     return swa::launch_combine(c, D, dtype, stream) == hipSuccess ? SWA_OK : SWA_ERR_HIP;
+}
+
+// Split decode launch, then the merge of its partials.  The bf16 kernel walks
+// sink entries within split 0 and, with a single split, writes the rows
+// itself; the f32 kernel gives the sinks a split of their own.
+int run_decode(DecodeParams& p, void* out, float* lse, int D, int dtype, bool paged,
+               hipStream_t stream) {
+    const bool bf16 = dtype == SWA_BF16;
+    p.splits = p.ring_splits + (!bf16 && !paged && p.n_sink > 0 ? 1 : 0);
+    if (bf16 && p.splits == 1) {
+        p.out = out;
+        p.lse = lse;
+    }
+    hipError_t e = bf16 ? swa::launch_decode_bf16(p, D, paged, stream)
+                        : swa::launch_decode_f32(p, D, paged, stream);
+    if (e != hipSuccess) return SWA_ERR_HIP;
+    if (p.out != nullptr) return SWA_OK;
+    return combine_decode(p, out, lse, D, dtype, stream);
 }
 
 // log2 of a power of two in [1, 2^20], else -1
@@ -262,10 +299,8 @@ int swa_fwd_cached(const void* q, const void* k, const void* v, const void* kcac
 
 size_t swa_decode_sinks_workspace_size(int B, int Hq, int W, int D, int n_sink) {
     if (B <= 0 || Hq <= 0 || W <= 0 || !supported_d(D) || n_sink < 0) return 0;
-    int splits, per;
-    decode_splits(B, Hq, W, &splits, &per);
-    splits += n_sink > 0 ? 1 : 0;  // the sink entries get a split of their own
-    return (size_t)B * Hq * splits * swa::partial_floats(D) * sizeof(float);
+    return (size_t)B * Hq * decode_max_splits(B, Hq, W, n_sink) * swa::partial_floats(D) *
+           sizeof(float);
 }
 
 size_t swa_decode_workspace_size(int B, int Hq, int W, int D) {
@@ -297,15 +332,11 @@ int swa_decode_sinks(const void* q, const void* kcache, const void* vcache,
     p.W = W;
     p.group = Hq / Hkv;
     p.scale_log2 = scale * kLog2e;
-    decode_splits(B, Hq, W, &p.ring_splits, &p.slots_per_split);
+    decode_splits(dtype, B, Hq, Hkv, W, &p.ring_splits, &p.slots_per_split);
     p.ksink = ksink;
     p.vsink = vsink;
     p.n_sink = n_sink;
-    p.splits = p.ring_splits + (n_sink > 0 ? 1 : 0);
-    hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, false, stream)
-                                     : swa::launch_decode_f32(p, D, false, stream);
-    if (e != hipSuccess) return SWA_ERR_HIP;
-    return combine_decode(p, out, lse, D, dtype, stream);
+    return run_decode(p, out, lse, D, dtype, false, stream);
 }
 
 int swa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ring_head,
@@ -362,17 +393,13 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
     p.W = W;
     p.group = Hq / Hkv;
     p.scale_log2 = scale * kLog2e;
-    decode_splits(B, Hq, W, &p.ring_splits, &p.slots_per_split);
-    p.splits = p.ring_splits;
+    decode_splits(dtype, B, Hq, Hkv, W, &p.ring_splits, &p.slots_per_split);
     p.block_table = block_table;
     p.seq_len = seq_len;
     p.n_pages = n_pages;
     p.page_shift = sh;
     p.nb = nb;
-    hipError_t e = dtype == SWA_BF16 ? swa::launch_decode_bf16(p, D, true, stream)
-                                     : swa::launch_decode_f32(p, D, true, stream);
-    if (e != hipSuccess) return SWA_ERR_HIP;
-    return combine_decode(p, out, lse, D, dtype, stream);
+    return run_decode(p, out, lse, D, dtype, true, stream);
 }
 
 // Workspace of swa_bwd: per-row dout . out, then (global tokens only) the

@@ -114,8 +114,13 @@ struct DecodeParams {
     const int32_t* ring_head;
     const int32_t* cache_len;
     float* partials;   // [B][Hq][splits][D+4]
+    // bf16 kernel with splits == 1: the rows are written here directly
+    // ([B][Hq][D], lse [B][Hq] or null) and no partials are made
+    void* out;
+    float* lse;
     int B, Hq, Hkv, W, group;
-    int splits;        // partials per row: ring splits, plus one for the sinks
+    int splits;        // partials per row: the ring splits, plus (f32 kernel) one
+                       // for the sinks; the bf16 kernel walks the sinks in split 0
     int ring_splits;   // splits over the ring's W slots
     int slots_per_split;
     float scale_log2;
