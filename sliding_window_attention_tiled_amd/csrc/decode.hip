@@ -492,25 +492,57 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(const DecodeParams p) {
 // ---- merge split partials ------------------------------------------------------------
 // One wave per output row: M = max m_s, L = sum l_s 2^(m_s - M),
 // out = sum acc_s 2^(m_s - M) / L, lse = (M + log2 L) ln 2.  A row with no keys
-// (L == 0) gets out = 0 and lse = -inf.
+// (L == 0) gets out = 0 and lse = -inf.  The (m, l) pairs are read one split
+// per lane and reduced across the wave; the acc records are read with eight
+// splits' loads in flight, each lane holding D / 64 dimensions.
 template <int D, typename OutT>
 __global__ __launch_bounds__(64) void combine_kernel(const CombineParams p) {
+    constexpr int RP = D + kPartialPad;  // floats per record
+    constexpr int U = 8;                 // splits per batch of loads
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
-    const float* rec0 = p.partials + (size_t)row * p.splits * (D + kPartialPad);
+    const float* rec0 = p.partials + (size_t)row * p.splits * RP;
     float M = kEmptyMax;
-    for (int s = 0; s < p.splits; s++) M = fmaxf(M, rec0[s * (D + kPartialPad) + D]);
+    for (int s = lane; s < p.splits; s += 64) M = fmaxf(M, rec0[(size_t)s * RP + D]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.f;
     float acc[D / 64];
 #pragma unroll
     for (int i = 0; i < D / 64; i++) acc[i] = 0.f;
-    for (int s = 0; s < p.splits; s++) {
-        const float* rec = rec0 + s * (D + kPartialPad);
-        const float f = fast_exp2(rec[D] - M);
-        L += f * rec[D + 1];
+    for (int s0 = 0; s0 < p.splits; s0 += 64) {
+        // weight of split s0 + lane, then its share of L
+        const int s = s0 + lane;
+        float f = 0.f;
+        if (s < p.splits) {
+            const float* rec = rec0 + (size_t)s * RP;
+            f = fast_exp2(rec[D] - M);
+            L += f * rec[D + 1];
+        }
+        const int n = min(64, p.splits - s0);
+        const float* base = rec0 + (size_t)s0 * RP + lane;
+        int t = 0;
+        for (; t + U <= n; t += U) {
+            float v[U][D / 64];
 #pragma unroll
-        for (int i = 0; i < D / 64; i++) acc[i] += f * rec[lane + i * 64];
+            for (int u = 0; u < U; u++)
+#pragma unroll
+                for (int i = 0; i < D / 64; i++) v[u][i] = base[(size_t)(t + u) * RP + i * 64];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const float fu = __shfl(f, t + u);
+#pragma unroll
+                for (int i = 0; i < D / 64; i++) acc[i] += fu * v[u][i];
+            }
+        }
+        for (; t < n; t++) {
+            const float fu = __shfl(f, t);
+#pragma unroll
+            for (int i = 0; i < D / 64; i++) acc[i] += fu * base[(size_t)t * RP + i * 64];
+        }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
     size_t out_off, lse_off;
     if (p.mode == 0) {
         out_off = (size_t)row * D;
