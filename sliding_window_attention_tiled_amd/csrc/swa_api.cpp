@@ -510,13 +510,15 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         gb.n_global = ng;
         for (int i = 0; i < ng; i++) gb.gpos[i] = g[i];
         gb.row_tiles = gb.key_tiles = (int)cdiv(ng, swa::kGlobalBwdItems);
-        // splits of the N keys (rows) so that each pass has about 2048 workgroups
+        // splits of the N keys (rows) so that each pass has about 512 workgroups:
+        // each split ends in float atomics of its 16 x D sums, so fewer,
+        // longer splits beat more parallelism here
         const int64_t nkc = std::min<int64_t>(
-            cdiv(N, 256), std::max<int64_t>(1, cdiv(2048, (int64_t)B * Hq * gb.row_tiles)));
+            cdiv(N, 256), std::max<int64_t>(1, cdiv(512, (int64_t)B * Hq * gb.row_tiles)));
         gb.key_chunk = (int)(cdiv(cdiv(N, nkc), 32) * 32);
         gb.n_key_chunks = (int)cdiv(N, gb.key_chunk);
         const int64_t nrc = std::min<int64_t>(
-            cdiv(N, 256), std::max<int64_t>(1, cdiv(2048, (int64_t)B * Hkv * gb.key_tiles)));
+            cdiv(N, 256), std::max<int64_t>(1, cdiv(512, (int64_t)B * Hkv * gb.key_tiles)));
         gb.row_chunk = (int)(cdiv(cdiv(N, nrc), 32) * 32);
         gb.n_row_chunks = (int)cdiv(N, gb.row_chunk);
         gb.n_row_tiles_all = gb.n_key_tiles_all = (int)cdiv(N, 64);
