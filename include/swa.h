@@ -213,8 +213,9 @@ int swa_fwd_cached(const void* q, const void* k, const void* v,
  *               each take one slot range writes the rows directly and leaves
  *               it untouched.  Two calls in flight at once must not share it.
  *
- * Errors: as swa_kv_append, plus SWA_ERR_ARG for Hq % Hkv != 0 and
- * SWA_ERR_WORKSPACE when the workspace is NULL or too small.
+ * Errors: as swa_kv_append, plus SWA_ERR_ARG for Hq % Hkv != 0 or sizes whose
+ * launch grid would pass 2^31 - 1 workgroups, and SWA_ERR_WORKSPACE when the
+ * workspace is NULL or too small.
  */
 int swa_decode(const void* q, const void* kcache, const void* vcache,
                const int32_t* ring_head, const int32_t* cache_len,

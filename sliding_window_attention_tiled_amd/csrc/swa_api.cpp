@@ -119,6 +119,11 @@ int run_decode(DecodeParams& p, void* out, float* lse, int D, int dtype, bool pa
                hipStream_t stream) {
     const bool bf16 = dtype == SWA_BF16;
     p.splits = p.ring_splits + (!bf16 && !paged && p.n_sink > 0 ? 1 : 0);
+    // grids: bf16 one workgroup per (b, kv head, 16-head block, split), float32
+    // one per (b, query head, split); the merge one per (b, query head)
+    const int64_t grid = bf16 ? (int64_t)p.B * p.Hkv * cdiv(p.group, 16) * p.splits
+                              : (int64_t)p.B * p.Hq * p.splits;
+    if (grid > INT32_MAX || (int64_t)p.B * p.Hq > INT32_MAX) return SWA_ERR_ARG;
     if (bf16 && p.splits == 1) {
         p.out = out;
         p.lse = lse;

@@ -130,6 +130,8 @@ def test_decode_validation(lib):
     assert call(dtype=3) == UNSUP
     assert call(ws=None) == WS
     assert call(wsb=need - 4) == WS
+    # a grid beyond 2^31 - 1 workgroups is refused before any launch
+    assert call(B=1 << 20, Hq=1 << 12, Hkv=1 << 12, wsb=(1 << 63)) == ARG
 
 
 def test_python_binding_requires_device_tensors(lib):
