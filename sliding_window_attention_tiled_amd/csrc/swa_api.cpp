@@ -527,7 +527,10 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         gb.row_chunk = (int)(cdiv(cdiv(N, nrc), 32) * 32);
         gb.n_row_chunks = (int)cdiv(N, gb.row_chunk);
         gb.n_row_tiles_all = gb.n_key_tiles_all = (int)cdiv(N, 64);
-        if ((int64_t)B * Hq * gb.n_row_tiles_all > INT32_MAX) return SWA_ERR_ARG;
+        if ((int64_t)B * Hq * gb.n_row_tiles_all > INT32_MAX ||
+            (int64_t)B * Hq * gb.row_tiles * gb.n_key_chunks > INT32_MAX ||
+            (int64_t)B * Hkv * gb.key_tiles * gb.n_row_chunks > INT32_MAX)
+            return SWA_ERR_ARG;
     }
 
     if (swa::launch_bwd_delta(bp, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
