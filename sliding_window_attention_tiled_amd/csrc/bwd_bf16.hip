@@ -383,6 +383,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
         st = min(st, n_steps - 1);
         const int hq = kvh * p.group + st / n_qt;
         const int q0 = q_lo + (st % n_qt) * BQ;
+        // lse for threads 0..63, delta for 64..127, one row each (later lanes
+        // read a row again and drop it, so the load needs no branch).  It is
+        // issued before the tile rows and used only when stored (lse scaled to
+        // base 2 there): any wait the compiler places around it, for a register
+        // kept in scratch say, then cannot include the tile loads, which would
+        // stall the step for their whole latency.
+        {
+            const int qrow = min(q0 + (int)(threadIdx.x & (BQ - 1)), q_hi);
+            const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
+            rl = *((threadIdx.x < BQ ? p.lse : bp.delta) + li);
+        }
         const int row0 = threadIdx.x / Q::CPR, cc = threadIdx.x % Q::CPR;
 #pragma unroll
         for (int u = 0; u < Q::PER_THREAD; u++) {
@@ -391,12 +402,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
                 (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
             qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
             gr[u] = *(const u32x4*)((const __bf16*)bp.dout + off);
-        }
-        // lse (base 2) for threads 0..63, delta for 64..127, one row each
-        if (threadIdx.x < 2 * BQ) {
-            const int qrow = min(q0 + (int)(threadIdx.x & (BQ - 1)), q_hi);
-            const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
-            rl = threadIdx.x < BQ ? p.lse[li] * kLog2e : bp.delta[li];
         }
     };
     auto store_step = [&](int stage) {
@@ -409,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
             *(u32x4*)(qs + rw * Q::QP + cc * 8) = qr[u];
             *(u32x4*)(gs + rw * Q::QP + cc * 8) = gr[u];
         }
-        if (threadIdx.x < 2 * BQ) rsm[stage][threadIdx.x] = rl;
+        if (threadIdx.x < 2 * BQ) rsm[stage][threadIdx.x] = threadIdx.x < BQ ? rl * kLog2e : rl;
     };
 
     const int tr_off = tr_row(lane) * Q::QP + tr_col(lane);
