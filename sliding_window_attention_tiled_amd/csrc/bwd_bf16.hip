@@ -168,63 +168,66 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
         const bool need_mask = !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
         const unsigned short* Ks = smem + st * T::STAGE;
         const unsigned short* Vs = Ks + T::K_ELEMS;
-        f32x16 s[2], dp[2];
-        if (!skip) {
-            // S^T = K Q^T and dP^T = V dout^T: two 32-key blocks each
-            s[0] = s[1] = dp[0] = dp[1] = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < KC; kc++) {
-                bf16x8 ka[2], va[2];
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    ka[kb] = *(const bf16x8*)(Ks + (kb * 32 + l32) * T::KP + kc * 16 + half * 8);
-                    va[kb] = *(const bf16x8*)(Vs + (kb * 32 + l32) * T::VP + kc * 16 + half * 8);
-                }
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb], qreg[kc], s[kb], 0, 0, 0);
-                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kb], greg[kc], dp[kb], 0, 0, 0);
-                }
-            }
-        }
-        if (has_next)
+        if (skip && has_next)
             load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, j + 1,
                                 gk_lds[st ^ 1], nullptr);
         if (!skip) {
-            if (need_mask) {
-                // the forward's band edge masks (x = key - query + wl in [0, wl + wr],
-                // key <= k_hi), integer arithmetic
-                const int base = kt0 + half * 4 - qres + p.wl;
-                const int sb = p.wl + p.wr - base;
-                const int lim = ks.k_hi - kt0 - half * 4;
+            // one 32-key block at a time: S^T = K Q^T and dP^T = V dout^T for
+            // its keys, then dS^T and dq^T += K^T dS^T over its two 16-key
+            // steps (half the score registers live at once)
 #pragma unroll
-                for (int kb = 0; kb < 2; kb++)
+            for (int kb = 0; kb < 2; kb++) {
+                f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                for (int kc = 0; kc < KC; kc++) {
+                    const bf16x8 ka =
+                        *(const bf16x8*)(Ks + (kb * 32 + l32) * T::KP + kc * 16 + half * 8);
+                    const bf16x8 va =
+                        *(const bf16x8*)(Vs + (kb * 32 + l32) * T::VP + kc * 16 + half * 8);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[kc], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, greg[kc], dp, 0, 0, 0);
+                }
+                // the next tile's loads go out after the first block's score MFMAs
+                // (issued before them, the compiler would wait for the loads
+                // ahead of the MFMAs, whose results may reuse their address
+                // registers)
+                if (kb == 0 && has_next)
+                    load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p,
+                                        j + 1, gk_lds[st ^ 1], nullptr);
+                if (need_mask) {
+                    // the forward's band edge masks (x = key - query + wl in
+                    // [0, wl + wr], key <= k_hi), integer arithmetic
+                    const int base = kt0 + half * 4 - qres + p.wl;
+                    const int sb = p.wl + p.wr - base;
+                    const int lim = ks.k_hi - kt0 - half * 4;
 #pragma unroll
                     for (int e = 0; e < 16; e++) {
                         const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
                         const int bad = ((base + ko) | (sb - ko) | (lim - ko)) >> 31;
-                        s[kb][e] += __builtin_bit_cast(float, bad & 0xff800000);
+                        s[e] += __builtin_bit_cast(float, bad & 0xff800000);
                     }
-            }
-            // dS^T = P^T (dP^T - delta), bf16, in the slot order of the K^T reads;
-            // then dq^T += K^T dS^T over four 16-key steps
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                bf16x8 ds;
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int ei = (t & 1) * 8 + slot_elem(e);
-                    const float pe = fast_exp2(__builtin_fmaf(s[t >> 1][ei], c, -lse2));
-                    ds[e] = (__bf16)(pe * (dp[t >> 1][ei] - dlt));
                 }
+                // dS^T = P^T (dP^T - delta), bf16, in the slot order of the K^T
+                // reads; then dq^T += K^T dS^T over this block's 16-key steps
 #pragma unroll
-                for (int db = 0; db < DB; db++) {
-                    const unsigned short* kp = Ks + tr_off + t * 16 * T::KP + tr_block_col(db);
-                    const i16x4 lo = lds_read_tr16(kp);
-                    const i16x4 hi = lds_read_tr16(kp + kTrHi * T::KP);
-                    const bf16x8 ka = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ds, dqacc[db], 0, 0, 0);
+                for (int t = 2 * kb; t < 2 * kb + 2; t++) {
+                    bf16x8 ds;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const int ei = (t & 1) * 8 + slot_elem(e);
+                        const float pe = fast_exp2(__builtin_fmaf(s[ei], c, -lse2));
+                        ds[e] = (__bf16)(pe * (dp[ei] - dlt));
+                    }
+#pragma unroll
+                    for (int db = 0; db < DB; db++) {
+                        const unsigned short* kp = Ks + tr_off + t * 16 * T::KP + tr_block_col(db);
+                        const i16x4 lo = lds_read_tr16(kp);
+                        const i16x4 hi = lds_read_tr16(kp + kTrHi * T::KP);
+                        const bf16x8 ka = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        dqacc[db] =
+                            __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ds, dqacc[db], 0, 0, 0);
+                    }
                 }
             }
         }
