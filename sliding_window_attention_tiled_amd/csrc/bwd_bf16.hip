@@ -477,11 +477,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
                 }
             }
         }
-        // next tile's rows into registers (stored at the end of the step).  The
-        // PAR = 1 copy issues them here; the PAR = 0 copy after phase 1, since
-        // at its score-phase register peak the compiler would otherwise move
-        // the fresh loads to other registers and wait for them on the spot.
-        if (PAR == 1) load_step(st + 2);
+        // next tile's rows into registers (stored at the end of the step).  At
+        // D = 128 the PAR = 0 copy issues them after phase 1 instead: at its
+        // score-phase register peak the compiler would otherwise move the
+        // fresh loads to other registers and wait for them on the spot.
+        constexpr bool late_load = D == 128 && PAR == 0;
+        if (!late_load) load_step(st + 2);
         const unsigned short* Qs = qsm[stage];
         const unsigned short* Qn = qsm[stage_next];
         const float* lse2 = rsm[stage];
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (PAR == 0) load_step(st + 2);
+        if (late_load) load_step(st + 2);
 
         // phase 2: dv^T += dout^T P and dk^T += Q^T dS over four 16-query steps
         TrFrag<D> tf[2];
