@@ -196,15 +196,18 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
                                         j + 1, gk_lds[st ^ 1], nullptr);
                 if (need_mask) {
                     // the forward's band edge masks (x = key - query + wl in
-                    // [0, wl + wr], key <= k_hi), integer arithmetic
+                    // [0, wl + wr], key <= k_hi): the lane's valid offsets form
+                    // one interval [lo, hi] (an empty one moved past the tile),
+                    // one unsigned range compare and a select per element
                     const int base = kt0 + half * 4 - qres + p.wl;
-                    const int sb = p.wl + p.wr - base;
-                    const int lim = ks.k_hi - kt0 - half * 4;
+                    int lo = -base;
+                    int hi = min(p.wl + p.wr - base, ks.k_hi - kt0 - half * 4);
+                    if (hi < lo) lo = hi = 1 << 20;
+                    const unsigned span = (unsigned)(hi - lo);
 #pragma unroll
                     for (int e = 0; e < 16; e++) {
                         const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
-                        const int bad = ((base + ko) | (sb - ko) | (lim - ko)) >> 31;
-                        s[e] += __builtin_bit_cast(float, bad & 0xff800000);
+                        if ((unsigned)(ko - lo) > span) s[e] = -INFINITY;
                     }
                 }
                 // dS^T = P^T (dP^T - delta), bf16, in the slot order of the K^T

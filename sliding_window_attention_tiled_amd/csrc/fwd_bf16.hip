@@ -210,19 +210,21 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
                     for (int qb = 0; qb < QB; qb++) {
                         // x = key - query + wl must lie in [0, wl + wr] and the key
-                        // must not pass k_hi; a negative x | (span - x) | (lim - ko)
-                        // flags a violation.  Integer arithmetic only, so the masks
-                        // need no scalar condition registers.
+                        // must not pass k_hi: for this lane the valid offsets ko
+                        // (less the lane's half * 4) form one interval [lo, hi], an
+                        // empty one moved past the tile.  Per element one
+                        // unsigned range compare and a select.
                         const int base = kt0 + half * 4 - qres[qb] + p.wl;
-                        const int sb = p.wl + p.wr - base;
-                        const int lim = ks.k_hi - kt0 - half * 4;
+                        int lo = -base;
+                        int hi = min(p.wl + p.wr - base, ks.k_hi - kt0 - half * 4);
+                        if (hi < lo) lo = hi = 1 << 20;
+                        const unsigned span = (unsigned)(hi - lo);
 #pragma unroll
                         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
                             for (int e = 0; e < 16; e++) {
                                 const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
-                                const int bad = ((base + ko) | (sb - ko) | (lim - ko)) >> 31;
-                                s[qb][kb][e] += __builtin_bit_cast(float, bad & 0xff800000);
+                                if ((unsigned)(ko - lo) > span) s[qb][kb][e] = -INFINITY;
                             }
                     }
                 } else {
