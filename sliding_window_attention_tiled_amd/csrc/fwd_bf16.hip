@@ -288,6 +288,11 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 m_run[qb] = m_use[qb];
             }
             // O^T += V^T P^T : four 16-key steps; V^T through transposing reads
+            // At D = 128 a wave takes issue priority over the other wave on its
+            // SIMD while it runs P V, so that the other wave's softmax work
+            // fills the gaps between these MFMAs rather than the reverse
+            // (2% faster there; 2% slower at D = 64, where P V is short).
+            if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
             const int key_l = half * 4 + ((lane & 15) >> 2);
             const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
@@ -335,6 +340,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 }
             }
         }
+        if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
         if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
     }
