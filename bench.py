@@ -69,6 +69,20 @@ def exact_pairs_causal(N: int, W: int) -> int:
     return full * W + ramp * (ramp + 1) // 2
 
 
+def dilated_causal_pairs(N: int, wl: int, d: int) -> int:
+    """Attended pairs of a causal dilated window: query i sees i, i - d, ...,
+    down to max(i - wl*d, i mod d)."""
+    return int((np.minimum(wl, np.arange(N) // d) + 1).sum())
+
+
+def prefill_pairs(n: int, wl: int, ring_len: int) -> int:
+    """Attended pairs of an n-token chunk after ring_len cached tokens, causal
+    window wl + 1: chunk token t sees min(ring_len, max(wl - t, 0)) ring entries
+    and chunk tokens max(0, t - wl) .. t."""
+    t = np.arange(n)
+    return int((np.minimum(ring_len, np.maximum(wl - t, 0)) + np.minimum(t, wl) + 1).sum())
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,9 +301,7 @@ def bench_other_workloads():
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     bytes_ = 4.0 * B * N * H * D * 2 + 4.0 * B * H * N
     for d in c["dilations"]:
-        # causal dilated band: i, i - d, ..., down to max(i - wl*d, i mod d)
-        pairs = (np.minimum(c["win_left"], np.arange(N) // d) + 1).sum()
-        flop = 4.0 * B * H * D * float(pairs)
+        flop = 4.0 * B * H * D * float(dilated_causal_pairs(N, c["win_left"], d))
         ms, mn = _time_calls(lambda: binding.fwd(q, k, v, win_left=c["win_left"], win_right=0,
                                                  dilation=d, out=out, lse=lse))
         res.append(_report(f"dilated_stack_d{d}", ms, mn, flop, bytes_))
@@ -305,10 +317,8 @@ def bench_other_workloads():
     length = torch.from_numpy(gen.cache_len.copy()).to("cuda")
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
-    t = np.arange(n)
     wl = c["win_left"]
-    pairs = (np.minimum(W, np.maximum(wl - t, 0)) + np.minimum(t, wl) + 1).sum()
-    flop = 4.0 * B * Hq * D * float(pairs)
+    flop = 4.0 * B * Hq * D * float(prefill_pairs(n, wl, W))
     bytes_ = (2.0 * B * n * Hq * D * 2 + 2.0 * B * n * Hkv * D * 2 + 2.0 * B * Hkv * W * D * 2
               + 4.0 * B * Hq * n)
     ms, mn = _time_calls(lambda: binding.fwd_cached(q, k, v, kc, vc, head, length,
