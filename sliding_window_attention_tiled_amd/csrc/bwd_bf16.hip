@@ -328,10 +328,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
     const int l32 = lane & 31;
     const int half = lane >> 5;
 
-    // work item: (b, kv head, residue class, key block); blocks of a slab from
-    // the last to the first, as in the forward
+    // work item: (b, kv head, residue class, key block); the longest blocks of
+    // a slab first.  A key block's query rows run off the end of the sequence
+    // when the window reaches further left than right (causal): those blocks
+    // are the short ones, so then the slab goes from the first block to the
+    // last (the mirror of the forward's order).  Workgroups that start
+    // together also stay in step, and read the same query tiles while L2
+    // still holds them.
     const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    int t = bp.ktiles_per_slab - 1 - L % bp.ktiles_per_slab;
+    const int Ls = L % bp.ktiles_per_slab;
+    int t = p.wl > p.wr ? Ls : bp.ktiles_per_slab - 1 - Ls;
     const int slab = L / bp.ktiles_per_slab;
     const int kvh = slab % p.Hkv;
     const int b = slab / p.Hkv;

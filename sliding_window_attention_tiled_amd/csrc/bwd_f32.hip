@@ -111,8 +111,12 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_f32_kernel(const BwdParams bp) {
     const int tid = threadIdx.x;
     const int part = tid & 3;
 
+    // longest key blocks first: from the first to the last when the window
+    // reaches further left than right (the last blocks' query rows run off the
+    // end of the sequence then), else from the last to the first
     const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-    int t = bp.ktiles_per_slab - 1 - L % bp.ktiles_per_slab;
+    const int Ls = L % bp.ktiles_per_slab;
+    int t = p.wl > p.wr ? Ls : bp.ktiles_per_slab - 1 - Ls;
     const int slab = L / bp.ktiles_per_slab;
     const int kvh = slab % p.Hkv;
     const int b = slab / p.Hkv;
