@@ -133,9 +133,28 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     // first gathered-key tile is loaded)
     if (!GROWS)
         for (int i = threadIdx.x; i < p.n_global; i += T::NT) gpos_lds[i] = p.gpos[i];
+    // With p.rotate the band tiles are walked in a rotated order: step j
+    // takes the band tile whose absolute index (k_lo / BN + tile) is j modulo
+    // the band's tile count.  Workgroups whose bands have the same length then
+    // read the same K/V tile at the same step, while it is in L2, instead of a
+    // few steps apart.  Gathered global-key tiles follow in order.
+    // (compiled only into the launches the host may rotate: four-wave
+    // workgroups at D = 128; the others keep the plain order at no cost)
+    constexpr bool kRotatable = !GROWS && D == 128 && NW == 4;
+    const int nbt = ks.n_band_tiles;
+    int rot = 0;
+    if (kRotatable && nbt > 0 && p.rotate) {
+        const int a = ks.k_lo >= 0 ? ks.k_lo / BN : -((-ks.k_lo + BN - 1) / BN);
+        rot = ((-a) % nbt + nbt) % nbt;
+    }
+    auto tile_at = [&](int j) {
+        if constexpr (!kRotatable) return j;
+        const int t = j + rot;   // < 2 * nbt for a band step
+        return j < nbt ? (t >= nbt ? t - nbt : t) : j;
+    };
     u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
     if (ks.n_tiles > 0) {
-        load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, 0,
+        load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, tile_at(0),
                             gk_lds[0], gpos_lds);
         store_tile<T>(kr, vr, smem);
     }
@@ -146,8 +165,9 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         const bool has_next = j + 1 < ks.n_tiles;
 
         // classify this tile for this wave (wave-uniform)
-        const bool band_tile = GROWS || j < ks.n_band_tiles;
-        const int kt0 = ks.k_lo + j * BN;
+        const int jt = tile_at(j);
+        const bool band_tile = GROWS || jt < ks.n_band_tiles;
+        const int kt0 = ks.k_lo + jt * BN;
         bool skip = false, need_mask = true;
         if (!GROWS && band_tile) {
             const int kt1 = kt0 + BN - 1;
@@ -194,8 +214,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         // (their results may reuse the loads' address registers).  The loads
         // then overlap the softmax and P V, and are stored after them.
         if (has_next)
-            load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p, j + 1,
-                                gk_lds[st ^ 1], gpos_lds);
+            load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p,
+                                tile_at(j + 1), gk_lds[st ^ 1], gpos_lds);
         if (!skip) {
             // Element masks.  Lane key offsets within the tile are
             // kb*32 + (e>>2)*8 + half*4 + (e&3); all compares are per element.
@@ -413,8 +433,19 @@ FwdShape fwd_bf16_shape(int group) {
     return FwdShape{hpw, rows, rows};
 }
 
-hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s) {
+hipError_t launch_fwd_bf16(const FwdParams& band, int D, hipStream_t s) {
+    FwdParams p = band;
     const bool w8 = waves_per_wg(p.hpw) == 8;
+    // In the natural order a workgroup reads a key tile bmq / BN steps after
+    // its neighbour did, and in between the workgroups running on one XCD (32
+    // CUs, one eight-wave or two four-wave workgroups each) read that many
+    // steps' tiles.  Where that reaches the XCD's 4 MB L2 the tile is fetched
+    // again, and the walk is rotated: four-wave workgroups of 128 positions at
+    // D = 128 (2 steps x 64 workgroups x 32 KB).  Below it the natural order
+    // already finds its tiles in L2 and is kept.
+    constexpr double kL2Bytes = 4.0 * 1024 * 1024;
+    const double reuse = (double)(p.bmq / BN) * (32 * (w8 ? 1 : 2)) * ((double)BN * D * 2 * 2);
+    p.rotate = reuse >= kL2Bytes;
     if (D == 128) return w8 ? launch_d<128, kQB, 8>(p, s) : launch_d<128, kQB, 4>(p, s);
     return w8 ? launch_d<64, kQB, 8>(p, s) : launch_d<64, kQB, 4>(p, s);
 }

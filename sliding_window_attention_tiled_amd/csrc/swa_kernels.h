@@ -44,6 +44,7 @@ struct FwdParams {
     int tiles_per_slab;           // all tiles of one (b, kv head, head group)
     int head_groups;              // group / hpw
     int n_blocks;                 // grid size of the band launch
+    int rotate;                   // bf16 band launch: walk band tiles rotated (set at launch)
     // global tokens (sorted, unique)
     int n_global;
     int g_chunk;       // keys per split of a global row
