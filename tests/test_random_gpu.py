@@ -2,8 +2,9 @@
 
 The hand-picked cases elsewhere pin each feature on its own; these draw them
 together (GQA group sizes 1 to 8, asymmetric and degenerate windows, dilation,
-duplicate and edge global tokens, both head dimensions and both dtypes) so
-that combinations nobody listed are exercised too.  The draws come from one
+duplicate and edge global tokens, both head dimensions and both dtypes; for
+the decode: batch, GQA group, ring size and fill) so that combinations nobody
+listed are exercised too.  The draws come from one
 fixed seed: every run checks the same shapes.
 """
 import numpy as np
@@ -12,7 +13,7 @@ import torch
 
 import oracle
 from sliding_window_attention_tiled_amd import binding
-from sliding_window_attention_tiled_amd.inputs import fwd_inputs
+from sliding_window_attention_tiled_amd.inputs import DecodeInputs, fwd_inputs
 from tests.gpu_util import check, log, to_dev, to_host_f64
 from tests.test_bwd_gpu import _check_grad
 
@@ -83,3 +84,33 @@ def test_bwd_random(case):
     _check_grad(to_host_f64(dq), rq, dt, f"{name} dq")
     _check_grad(to_host_f64(dk), rk, dt, f"{name} dk")
     _check_grad(to_host_f64(dv), rv, dt, f"{name} dv")
+
+
+def _draw_decode(n_cases, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for c in range(n_cases):
+        Hkv = int(rng.choice([1, 2, 4]))
+        group = int(rng.choice([1, 2, 4, 8, 16]))
+        B = int(rng.integers(1, 7))
+        W = int(rng.integers(1, 1201))
+        D = int(rng.choice([64, 128]))
+        dt = "f32" if rng.random() < 0.2 else "bf16"
+        u = rng.random()
+        fill = None if u < 0.4 else (0 if u < 0.55 else int(rng.integers(0, W + 1)))
+        cases.append((f"d{c}", B, group * Hkv, Hkv, W, D, dt, fill))
+    return cases
+
+
+# ring sizes up to 1200 and batches of 1 to 6 take the decode through one and
+# through many slot ranges per (sequence, kv head), and through the combine
+DECODE_CASES = _draw_decode(16, 20261205)
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_random(case):
+    from tests.test_decode_gpu import _run_steps
+    name, B, Hq, Hkv, W, D, dt, fill = case
+    log(f"[decode random] {case}")
+    gen = DecodeInputs(3000 + int(name[1:]), B, Hq, Hkv, W, D, dt, fill=fill)
+    _run_steps(gen, 5, set(range(5)), dt, name)
