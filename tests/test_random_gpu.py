@@ -3,7 +3,8 @@
 The hand-picked cases elsewhere pin each feature on its own; these draw them
 together (GQA group sizes 1 to 8, asymmetric and degenerate windows, dilation,
 duplicate and edge global tokens, both head dimensions and both dtypes; for
-the decode: batch, GQA group, ring size and fill) so that combinations nobody
+the decode and the chunked prefill: batch, GQA group, ring size and fill,
+chunk length and window) so that combinations nobody
 listed are exercised too.  The draws come from one
 fixed seed: every run checks the same shapes.
 """
@@ -114,3 +115,43 @@ def test_decode_random(case):
     log(f"[decode random] {case}")
     gen = DecodeInputs(3000 + int(name[1:]), B, Hq, Hkv, W, D, dt, fill=fill)
     _run_steps(gen, 5, set(range(5)), dt, name)
+
+
+def _draw_cached(n_cases, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for c in range(n_cases):
+        Hkv = int(rng.choice([1, 2]))
+        group = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, 4))
+        W = int(rng.integers(1, 601))
+        D = int(rng.choice([64, 128]))
+        dt = "f32" if rng.random() < 0.2 else "bf16"
+        u = rng.random()
+        fill = None if u < 0.4 else (0 if u < 0.55 else int(rng.integers(0, W + 1)))
+        n = int(rng.integers(1, 501))
+        wl = int(rng.integers(0, W + 1))       # a chunk's window fits the ring: wl <= W
+        cases.append((f"c{c}", B, group * Hkv, Hkv, W, D, dt, fill, n, wl))
+    return cases
+
+
+CACHED_CASES = _draw_cached(12, 20261206)
+
+
+@pytest.mark.parametrize("case", CACHED_CASES, ids=[c[0] for c in CACHED_CASES])
+def test_fwd_cached_random(case):
+    name, B, Hq, Hkv, W, D, dt, fill, n, wl = case
+    log(f"[fwd_cached random] {case}")
+    seed = 4000 + int(name[1:])
+    gen = DecodeInputs(seed, B, 1, Hkv, W, D, dt, fill=fill)
+    q, k, v = fwd_inputs(seed + 500, B, Hq, Hkv, n, D, dt)
+    kc, vc = to_dev(gen.kcache), to_dev(gen.vcache)
+    head = torch.from_numpy(gen.ring_head.copy()).to("cuda")
+    length = torch.from_numpy(gen.cache_len.copy()).to("cuda")
+    out, lse = binding.fwd_cached(to_dev(q), to_dev(k), to_dev(v), kc, vc, head, length,
+                                  win_left=wl)
+    torch.cuda.synchronize()
+    ring = oracle.ring(gen.kcache, gen.vcache, gen.ring_head, gen.cache_len)
+    ref_o, ref_l = ring.fwd_cached(q, k, v, win_left=wl)
+    check(to_host_f64(out), ref_o, dt, f"{name} out")
+    check(to_host_f64(lse), ref_l, dt, f"{name} lse")
