@@ -3,8 +3,8 @@
 The hand-picked cases elsewhere pin each feature on its own; these draw them
 together (GQA group sizes 1 to 8, asymmetric and degenerate windows, dilation,
 duplicate and edge global tokens, both head dimensions and both dtypes; for
-the decode and the chunked prefill: batch, GQA group, ring size and fill,
-chunk length and window) so that combinations nobody
+the decode, with and without sinks, and the chunked prefill: batch, GQA
+group, ring size and fill, sink count, chunk length and window) so that combinations nobody
 listed are exercised too.  The draws come from one
 fixed seed: every run checks the same shapes.
 """
@@ -155,3 +155,32 @@ def test_fwd_cached_random(case):
     ref_o, ref_l = ring.fwd_cached(q, k, v, win_left=wl)
     check(to_host_f64(out), ref_o, dt, f"{name} out")
     check(to_host_f64(lse), ref_l, dt, f"{name} lse")
+
+
+SINK_CASES = [(f"s{c[0][1:]}",) + c[1:] + (int(n),) for c, n in zip(
+    _draw_decode(12, 20261207),
+    np.random.Generator(np.random.PCG64(20261208)).integers(0, 20, 12))]
+
+
+@pytest.mark.parametrize("case", SINK_CASES, ids=[c[0] for c in SINK_CASES])
+def test_decode_sinks_random(case):
+    from tests.test_sinks_gpu import _sinks
+    name, B, Hq, Hkv, W, D, dt, fill, S = case
+    log(f"[decode_sinks random] {case}")
+    seed = 5000 + int(name[1:])
+    gen = DecodeInputs(seed, B, Hq, Hkv, W, D, dt, fill=fill)
+    ks, vs = _sinks(seed + 500, B, Hkv, S, D, dt)
+    kc, vc = to_dev(gen.kcache), to_dev(gen.vcache)
+    head = torch.from_numpy(gen.ring_head.copy()).to("cuda")
+    length = torch.from_numpy(gen.cache_len.copy()).to("cuda")
+    ksd, vsd = to_dev(ks), to_dev(vs)
+    ring = oracle.ring(gen.kcache, gen.vcache, gen.ring_head, gen.cache_len)
+    for t in range(3):
+        qn, kn, vn = gen.step()
+        binding.kv_append(kc, vc, to_dev(kn), to_dev(vn), head, length)
+        out, lse = binding.decode_sinks(to_dev(qn), kc, vc, head, length, ksd, vsd)
+        torch.cuda.synchronize()
+        ring.append(kn, vn)
+        ref_o, ref_l = ring.decode(qn, sinks=(ks, vs))
+        check(to_host_f64(out), ref_o, dt, f"{name} step {t} out")
+        check(to_host_f64(lse), ref_l, dt, f"{name} step {t} lse")
