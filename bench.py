@@ -7,7 +7,9 @@ nominal count 4*B*Hq*N*W*D per call; the exact count (sum over rows of the
 attended keys times 4*D) is reported beside it and is what the roofline
 fraction uses.  The same JSON line carries the decode leg (64 sequences,
 Hq=32, Hkv=8, D=128, W=4096 ring, append + attend per step) as HBM GB/s of
-K+V streamed, and the fp64 CPU oracle timed on a bounded sample of rows.
+K+V streamed, and the fp64 CPU oracle timed on bounded samples of both
+(forward rows as TFLOP/s, decode steps as GB/s), with the host's CPU count
+and model.
 
 Also reported, per call: the bidirectional encoder with global tokens, the
 four layers of the dilated stack and one 4096-token chunk of a chunked prefill
@@ -92,7 +94,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the per-call timings of the other workloads")
-    ap.add_argument("--cpu-rows", type=int, default=196608)
+    ap.add_argument("--cpu-rows", type=int, default=393216)
+    ap.add_argument("--cpu-decode-steps", type=int, default=256)
     ap.add_argument("--only", choices=["fwd", "decode", "others"], default=None,
                     help="run one leg only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -206,13 +209,15 @@ def bench_decode(args):
     dec_ms = float(np.mean([a.elapsed_time(b) for _, a, b in ev]))
     step_ms = float(np.mean([a.elapsed_time(b) for a, _, b in ev]))
     kv_bytes = 2.0 * c["B"] * c["Hkv"] * c["W"] * c["D"] * 2
+    host = dict(kcache=gen.kcache, vcache=gen.vcache, ring_head=gen.ring_head,
+                cache_len=gen.cache_len, q=qs, k=ks, v=vs)
     return dict(workload="rolling_cache_decode", B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], W=c["W"],
                 D=c["D"], steps=steps, ms_per_step_wall=wall * 1e3 / steps,
                 ms_append_plus_decode=step_ms, ms_decode=dec_ms,
                 kv_bytes_per_step=kv_bytes,
                 decode_gbs=kv_bytes / (dec_ms * 1e-3) / 1e9,
                 decode_frac_hbm=kv_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9)
+                step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9), host
 
 
 def _time_calls(fn, reps=10, warmup=3):
@@ -443,8 +448,11 @@ def bench_decode_variants():
 
 
 def cpu_baseline(inputs, cfg, n_rows):
+    """The oracle (built here with -O3 -march=native, OpenMP over rows) on a
+    seeded uniform sample of the forward's rows, as exact TFLOP/s."""
     import oracle
 
+    orc = oracle.native()
     qh, kh, vh = inputs
     N, Hq, B = cfg["N"], cfg["Hq"], cfg["B"]
     rng = np.random.Generator(np.random.PCG64(99))
@@ -453,13 +461,42 @@ def cpu_baseline(inputs, cfg, n_rows):
     W = cfg["win_left"] + 1
     pairs = np.minimum(rows[:, 2] + 1, W).sum()
     t0 = time.perf_counter()
-    oracle.fwd_rows(qh, kh, vh, rows, win_left=cfg["win_left"], win_right=cfg["win_right"])
+    orc.fwd_rows(qh, kh, vh, rows, win_left=cfg["win_left"], win_right=cfg["win_right"])
     dt = time.perf_counter() - t0
     flop = 4.0 * cfg["D"] * float(pairs)
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n_rows} seeded uniform (b, h, i) rows of the same workload, "
-                      f"exact in-window flop / wall time ({dt:.1f} s)"}
+    r = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+         "kind": "oracle",
+         "sample": f"{n_rows} seeded uniform (b, h, i) rows of the same workload, "
+                   f"exact in-window flop / wall time ({dt:.1f} s)",
+         "build": "gcc -O3 -march=native -fopenmp, fp64"}
+    r.update(oracle.host_info())
+    return r
+
+
+def cpu_baseline_decode(host, n_steps):
+    """The oracle's ring (append, then attend over the valid slots) on the first
+    n_steps steps of the decode workload's stream, as K+V GB/s: the K+V bytes
+    a step attends over (the whole 4096-slot ring of every sequence and kv
+    head) divided by the wall time per step."""
+    import oracle
+
+    orc = oracle.native()
+    ring = orc.ring(host["kcache"], host["vcache"], host["ring_head"], host["cache_len"])
+    B, Hkv, W, D = host["kcache"].shape
+    n = min(n_steps, len(host["q"]))
+    t0 = time.perf_counter()
+    for t in range(n):
+        ring.append(host["k"][t], host["v"][t])
+        ring.decode(host["q"][t])
+    dt = time.perf_counter() - t0
+    kv_bytes = 2.0 * B * Hkv * W * D * 2
+    r = {"value": kv_bytes * n / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(),
+         "kind": "oracle",
+         "sample": f"steps 0..{n - 1} of the 256-step rolling-cache stream (append + decode "
+                   f"each), {kv_bytes:.4g} B of K+V per step / wall time ({dt:.1f} s)",
+         "build": "gcc -O3 -march=native -fopenmp, fp64"}
+    r.update(oracle.host_info())
+    return r
 
 
 def main():
@@ -477,7 +514,7 @@ def main():
         copy_calibration()
         return
     if args.only == "decode":
-        print(json.dumps({"decode": bench_decode(args)}))
+        print(json.dumps({"decode": bench_decode(args)[0]}))
         return
     if args.only == "others":
         print(json.dumps({"other_workloads": bench_other_workloads()}))
@@ -507,12 +544,15 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(exact_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic()},
     }
+    dec_host = None
     if not args.no_decode and args.only is None:
-        res["decode"] = bench_decode(args)
+        res["decode"], dec_host = bench_decode(args)
     if not args.no_others and args.only is None:
         res["other_workloads"] = bench_other_workloads()
     if not args.no_cpu and args.only is None:
         res["cpu_baseline"] = cpu_baseline(f["inputs"], f["cfg"], args.cpu_rows)
+        if dec_host is not None:
+            res["cpu_baseline_decode"] = cpu_baseline_decode(dec_host, args.cpu_decode_steps)
     print(json.dumps(res))
 
 

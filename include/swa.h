@@ -43,6 +43,10 @@
  *     (SWA_F32 or SWA_BF16).  Accumulation is float32.  In bf16 the softmax
  *     weights are rounded to bf16 (nearest even) before the weighted sum of v.
  *   - D must be 64 or 128.
+ *   - `scale` (every entry point that takes one) is the softmax temperature
+ *     that multiplies q.k: it must be positive and finite (so must scale *
+ *     log2(e)); zero, negative, infinite or NaN scales give SWA_ERR_ARG.  The
+ *     scaled scores themselves must stay within float32 range.
  *   - Device pointers are caller-owned device memory.  The library allocates
  *     nothing and keeps no state between calls; all work is enqueued on
  *     `stream` (0 = the null stream) and nothing synchronises the host.
@@ -93,7 +97,8 @@ enum {
  *               duplicates, any order); NULL when n_global == 0.  At most
  *               SWA_MAX_GLOBAL distinct positions.  The array is read during
  *               the call only.
- *   scale       multiplier of q.k (1/sqrt(D) for the usual softmax_scale)
+ *   scale       multiplier of q.k (1/sqrt(D) for the usual softmax_scale);
+ *               positive and finite
  *   workspace   device scratch of at least swa_fwd_workspace_size(...) bytes,
  *               caller-owned, contents on entry irrelevant; used only when
  *               there are global positions (partial results of the global
@@ -103,7 +108,8 @@ enum {
  * Errors: SWA_ERR_ARG for null q/k/v/out, non-positive sizes, N > SWA_MAX_N,
  * Hq % Hkv != 0,
  * negative windows, dilation < 1, a global index outside [0, N), n_global < 0
- * or global_idx NULL with n_global > 0; SWA_ERR_UNSUPPORTED for D not in
+ * or global_idx NULL with n_global > 0, or a scale that is not positive and
+ * finite; SWA_ERR_UNSUPPORTED for D not in
  * {64,128}, an unknown dtype or more than SWA_MAX_GLOBAL distinct globals;
  * SWA_ERR_WORKSPACE when globals are present and the workspace is NULL or
  * smaller than swa_fwd_workspace_size(); SWA_ERR_HIP if a launch fails.
@@ -186,8 +192,9 @@ int swa_kv_append_chunk(void* kcache, void* vcache, const void* k, const void* v
  *   scale       multiplier of q.k (1/sqrt(D) for the usual scaling)
  *
  * Errors: SWA_ERR_ARG for null pointers (lse excepted), non-positive sizes,
- * n or W above SWA_MAX_N, Hq % Hkv != 0, win_left < 0 or win_left > W;
- * SWA_ERR_UNSUPPORTED for D or dtype; SWA_ERR_HIP if a launch fails.
+ * n or W above SWA_MAX_N, Hq % Hkv != 0, win_left < 0 or win_left > W, or a
+ * scale that is not positive and finite; SWA_ERR_UNSUPPORTED for D or dtype;
+ * SWA_ERR_HIP if a launch fails.
  */
 int swa_fwd_cached(const void* q, const void* k, const void* v,
                    const void* kcache, const void* vcache,
@@ -213,9 +220,9 @@ int swa_fwd_cached(const void* q, const void* k, const void* v,
  *               each take one slot range writes the rows directly and leaves
  *               it untouched.  Two calls in flight at once must not share it.
  *
- * Errors: as swa_kv_append, plus SWA_ERR_ARG for Hq % Hkv != 0 or sizes whose
- * launch grid would pass 2^31 - 1 workgroups, and SWA_ERR_WORKSPACE when the
- * workspace is NULL or too small.
+ * Errors: as swa_kv_append, plus SWA_ERR_ARG for Hq % Hkv != 0, a scale that
+ * is not positive and finite, or sizes whose launch grid would pass 2^31 - 1
+ * workgroups, and SWA_ERR_WORKSPACE when the workspace is NULL or too small.
  */
 int swa_decode(const void* q, const void* kcache, const void* vcache,
                const int32_t* ring_head, const int32_t* cache_len,
@@ -309,8 +316,9 @@ int swa_kv_append_paged(void* kpool, void* vpool, const void* k, const void* v,
  *   workspace of at least swa_decode_workspace_size(B, Hq, W, D) bytes.
  * A sequence with seq_len == 0 gets out = 0, lse = -inf.
  *
- * Errors: as swa_kv_append_paged, plus SWA_ERR_ARG for Hq % Hkv != 0 and
- * SWA_ERR_WORKSPACE when the workspace is NULL or too small.
+ * Errors: as swa_kv_append_paged, plus SWA_ERR_ARG for Hq % Hkv != 0 or a
+ * scale that is not positive and finite, and SWA_ERR_WORKSPACE when the
+ * workspace is NULL or too small.
  */
 int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
                      const int32_t* block_table, const int32_t* seq_len,

@@ -29,16 +29,42 @@ DT_F32 = 0
 DT_BF16 = 1
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
-    """Compile the oracle C source into a shared library with gcc (OpenMP, -O2)."""
+_LIB_NATIVE = os.path.join(_LIB_DIR, "libswa_oracle_native.so")
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB, native: bool = False) -> str:
+    """Compile the oracle C source into a shared library with gcc (OpenMP, -O3).
+
+    native=True adds -march=native: code for the CPU this runs on, which is
+    only safe to load on that machine (the CPU-baseline timing builds such a
+    copy where it runs; the default copy stays portable)."""
     os.makedirs(os.path.dirname(out), exist_ok=True)
     if force or not os.path.exists(out):
-        tmp = out + ".tmp"
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O3", *(["-march=native"] if native else []), "-fopenmp", "-fPIC",
+               "-shared", "-std=c11", "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)
     return out
+
+
+def host_info() -> dict:
+    """The host the oracle runs on: logical CPUs, the CPUs this process may
+    use, and the CPU model name."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
 
 
 def _ptr(a):
@@ -375,6 +401,20 @@ def default() -> OracleLib:
             build(force=True)
         _default = OracleLib(_LIB)
     return _default
+
+
+_native = None
+
+
+def native() -> OracleLib:
+    """A copy of the oracle built here with -march=native (rebuilt once per
+    process, for the machine it runs on).  Same source, same arithmetic: used
+    to time the oracle as a CPU baseline."""
+    global _native
+    if _native is None:
+        build(force=True, out=_LIB_NATIVE, native=True)
+        _native = OracleLib(_LIB_NATIVE)
+    return _native
 
 
 def num_threads() -> int:

@@ -100,6 +100,27 @@ def _dev(t: torch.Tensor | None, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _buffer(t: torch.Tensor | None, name: str, shape, dtype, like: torch.Tensor):
+    """A caller-supplied tensor the call reads or writes must have exactly the
+    shape, dtype and device the call assumes: the C ABI receives bare pointers
+    and cannot check them, so a wrong buffer would be an out-of-bounds device
+    access.  Checked before any launch (and before the device check of _dev)."""
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != like.device:
+        raise SwaError(-1, f"{name} must be {dtype} {tuple(shape)} on {like.device}; got "
+                           f"{t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def _same(ref: torch.Tensor, **tensors):
+    """Inputs that share the reference tensor's dtype and device."""
+    for name, t in tensors.items():
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise SwaError(-1, f"{name} must be {ref.dtype} on {ref.device}; got {t.dtype} on "
+                               f"{t.device}")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -124,9 +145,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, win_left: int,
     if k.shape != (B, N, Hkv, D) or v.shape != k.shape:
         raise SwaError(-1, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
                            f"v{tuple(v.shape)}")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise SwaError(-1, "q, k and v must share one dtype")
+    _same(q, k=k, v=v)
     dt = _dtype_code(q)
+    _buffer(out, "out", q.shape, q.dtype, q)
+    _buffer(lse, "lse", (B, Hq, N), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -143,6 +165,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, win_left: int,
         need = fwd_workspace_size(B, Hq, N, D, ng)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        elif workspace.device != q.device:
+            raise SwaError(-1, f"workspace must be on {q.device}")
         ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.swa_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
                      _dev(lse, "lse"), B, Hq, Hkv, N, D, win_left, win_right, dilation,
@@ -160,7 +184,8 @@ def kv_append(kcache: torch.Tensor, vcache: torch.Tensor, k_new: torch.Tensor,
     B, Hkv, W, D = kcache.shape
     if vcache.shape != kcache.shape or k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D):
         raise SwaError(-1, "kv_append shape mismatch")
-    _ring_state(ring_head, cache_len, B)
+    _same(kcache, vcache=vcache, k_new=k_new, v_new=v_new)
+    _ring_state(ring_head, cache_len, B, kcache)
     st = lib.swa_kv_append(_dev(kcache, "kcache"), _dev(vcache, "vcache"),
                            _dev(k_new, "k_new"), _dev(v_new, "v_new"),
                            _dev(ring_head, "ring_head"), _dev(cache_len, "cache_len"),
@@ -168,10 +193,10 @@ def kv_append(kcache: torch.Tensor, vcache: torch.Tensor, k_new: torch.Tensor,
     _check(st, "swa_kv_append")
 
 
-def _ring_state(ring_head: torch.Tensor, cache_len: torch.Tensor, B: int):
+def _ring_state(ring_head: torch.Tensor, cache_len: torch.Tensor, B: int, like: torch.Tensor):
     for t, name in ((ring_head, "ring_head"), (cache_len, "cache_len")):
-        if t.dtype != torch.int32 or t.shape != (B,):
-            raise SwaError(-1, f"{name} must be int32 [B]")
+        if t.dtype != torch.int32 or t.shape != (B,) or t.device != like.device:
+            raise SwaError(-1, f"{name} must be int32 [B] on {like.device}")
 
 
 def kv_append_chunk(kcache: torch.Tensor, vcache: torch.Tensor, k: torch.Tensor,
@@ -183,9 +208,8 @@ def kv_append_chunk(kcache: torch.Tensor, vcache: torch.Tensor, k: torch.Tensor,
     n = k.shape[1]
     if vcache.shape != kcache.shape or k.shape != (B, n, Hkv, D) or v.shape != k.shape:
         raise SwaError(-1, "kv_append_chunk shape mismatch")
-    if k.dtype != kcache.dtype or v.dtype != kcache.dtype:
-        raise SwaError(-1, "chunk and ring must share one dtype")
-    _ring_state(ring_head, cache_len, B)
+    _same(kcache, vcache=vcache, k=k, v=v)
+    _ring_state(ring_head, cache_len, B, kcache)
     st = lib.swa_kv_append_chunk(_dev(kcache, "kcache"), _dev(vcache, "vcache"), _dev(k, "k"),
                                  _dev(v, "v"), _dev(ring_head, "ring_head"),
                                  _dev(cache_len, "cache_len"), B, Hkv, W, n, D,
@@ -207,10 +231,10 @@ def fwd_cached(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kcache: torch.
         raise SwaError(-1, "fwd_cached chunk shape mismatch")
     if kcache.shape != (B, Hkv, W, D) or vcache.shape != kcache.shape:
         raise SwaError(-1, "fwd_cached ring shape mismatch")
-    for t in (k, v, kcache, vcache):
-        if t.dtype != q.dtype:
-            raise SwaError(-1, "q, k, v and the ring must share one dtype")
-    _ring_state(ring_head, cache_len, B)
+    _same(q, k=k, v=v, kcache=kcache, vcache=vcache)
+    _ring_state(ring_head, cache_len, B, q)
+    _buffer(out, "out", q.shape, q.dtype, q)
+    _buffer(lse, "lse", (B, Hq, n), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
@@ -240,11 +264,17 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
     Hkv, W = kcache.shape[1], kcache.shape[2]
     if kcache.shape != (B, Hkv, W, D) or vcache.shape != kcache.shape:
         raise SwaError(-1, "decode shape mismatch")
+    _same(q, kcache=kcache, vcache=vcache)
+    _ring_state(ring_head, cache_len, B, q)
+    _buffer(out, "out", q.shape, q.dtype, q)
+    _buffer(lse, "lse", (B, Hq), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = decode_workspace_size(B, Hq, W, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device:
+        raise SwaError(-1, f"workspace must be on {q.device}")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -276,15 +306,17 @@ def decode_sinks(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
         raise SwaError(-1, "decode_sinks ring shape mismatch")
     if ksink.shape != (B, Hkv, S, D) or vsink.shape != ksink.shape:
         raise SwaError(-1, "decode_sinks sink shape mismatch")
-    for t in (kcache, vcache, ksink, vsink):
-        if t.dtype != q.dtype:
-            raise SwaError(-1, "q, the ring and the sinks must share one dtype")
-    _ring_state(ring_head, cache_len, B)
+    _same(q, kcache=kcache, vcache=vcache, ksink=ksink, vsink=vsink)
+    _ring_state(ring_head, cache_len, B, q)
+    _buffer(out, "out", q.shape, q.dtype, q)
+    _buffer(lse, "lse", (B, Hq), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = decode_sinks_workspace_size(B, Hq, W, D, S)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device:
+        raise SwaError(-1, f"workspace must be on {q.device}")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -302,12 +334,14 @@ def decode_sinks(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
 
 
 def _paged_state(kpool, vpool, block_table, seq_len, B):
-    if vpool.shape != kpool.shape or vpool.dtype != kpool.dtype:
+    if vpool.shape != kpool.shape:
         raise SwaError(-1, "kpool and vpool must match")
-    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
-        raise SwaError(-1, "block_table must be int32 [B, nb]")
-    if seq_len.dtype != torch.int32 or seq_len.shape != (B,):
-        raise SwaError(-1, "seq_len must be int32 [B]")
+    _same(kpool, vpool=vpool)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+            block_table.shape[0] != B or block_table.device != kpool.device:
+        raise SwaError(-1, f"block_table must be int32 [B, nb] on {kpool.device}")
+    if seq_len.dtype != torch.int32 or seq_len.shape != (B,) or seq_len.device != kpool.device:
+        raise SwaError(-1, f"seq_len must be int32 [B] on {kpool.device}")
 
 
 def kv_append_paged(kpool: torch.Tensor, vpool: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -316,8 +350,9 @@ def kv_append_paged(kpool: torch.Tensor, vpool: torch.Tensor, k: torch.Tensor, v
     lib = load_library()
     n_pages, Hkv, P, D = kpool.shape
     B, n = k.shape[0], k.shape[1]
-    if k.shape != (B, n, Hkv, D) or v.shape != k.shape or k.dtype != kpool.dtype:
-        raise SwaError(-1, "kv_append_paged shape or dtype mismatch")
+    if k.shape != (B, n, Hkv, D) or v.shape != k.shape:
+        raise SwaError(-1, "kv_append_paged shape mismatch")
+    _same(kpool, k=k, v=v)
     _paged_state(kpool, vpool, block_table, seq_len, B)
     st = lib.swa_kv_append_paged(_dev(kpool, "kpool"), _dev(vpool, "vpool"),
                                  _dev(k, "k") if n else None, _dev(v, "v") if n else None,
@@ -336,14 +371,19 @@ def decode_paged(q: torch.Tensor, kpool: torch.Tensor, vpool: torch.Tensor,
     lib = load_library()
     B, Hq, D = q.shape
     n_pages, Hkv, P, _ = kpool.shape
-    if kpool.shape[3] != D or kpool.dtype != q.dtype:
-        raise SwaError(-1, "decode_paged shape or dtype mismatch")
+    if kpool.shape[3] != D:
+        raise SwaError(-1, "decode_paged shape mismatch")
+    _same(q, kpool=kpool)
     _paged_state(kpool, vpool, block_table, seq_len, B)
+    _buffer(out, "out", q.shape, q.dtype, q)
+    _buffer(lse, "lse", (B, Hq), torch.float32, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = decode_workspace_size(B, Hq, window, D)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device:
+        raise SwaError(-1, f"workspace must be on {q.device}")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -376,11 +416,11 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, ls
     if k.shape != (B, N, Hkv, D) or v.shape != k.shape or out.shape != q.shape or \
             dout.shape != q.shape or lse.shape != (B, Hq, N):
         raise SwaError(-1, "bwd shape mismatch")
-    for t in (k, v, out, dout):
-        if t.dtype != q.dtype:
-            raise SwaError(-1, "q, k, v, out and dout must share one dtype")
-    if lse.dtype != torch.float32:
-        raise SwaError(-1, "lse must be float32")
+    _same(q, k=k, v=v, out=out, dout=dout)
+    _buffer(lse, "lse", (B, Hq, N), torch.float32, q)
+    _buffer(dq, "dq", q.shape, q.dtype, q)
+    _buffer(dk, "dk", k.shape, k.dtype, q)
+    _buffer(dv, "dv", v.shape, v.dtype, q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dq = torch.empty_like(q) if dq is None else dq
@@ -393,6 +433,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, ls
     need = bwd_workspace_size(B, Hq, Hkv, N, D, ng)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device:
+        raise SwaError(-1, f"workspace must be on {q.device}")
     st = lib.swa_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
                      _dev(lse, "lse"), _dev(dout, "dout"), _dev(dq, "dq"), _dev(dk, "dk"),
                      _dev(dv, "dv"), B, Hq, Hkv, N, D, win_left, win_right, dilation, g, ng,

@@ -319,15 +319,24 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             for (int db = 0; db < DB; db++) oacc[db] *= alpha;
         }
         m_run = m_use;
+        // weights rounded to bf16 (the B operand of P V); the running sum adds
+        // those rounded weights, so out is normalised by exactly the weights
+        // it was built from, as in the forward
         bf16x8 pb;
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
+            for (int e = 0; e < 4; e++)
+                pb[kb * 4 + e] = (__bf16)fast_exp2(__builtin_fmaf(sc[kb][e], c, -m_use));
+        {
+            const __bf16 one = (__bf16)1.0f;
+            const bf16x2 ones = {one, one};
+#pragma unroll
             for (int e = 0; e < 4; e++) {
-                const float pe = fast_exp2(__builtin_fmaf(sc[kb][e], c, -m_use));
-                l_run += pe;
-                pb[kb * 4 + e] = (__bf16)pe;
+                const bf16x2 pr = {pb[2 * e], pb[2 * e + 1]};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
             }
+        }
         // O^T += V^T P^T: slot (grp*8 + t) of the B operand is key grp*4 + t (t < 4)
         // or 16 + grp*4 + (t - 4); V^T comes from transposing LDS reads.
 #pragma unroll

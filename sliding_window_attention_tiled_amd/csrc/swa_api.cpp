@@ -2,6 +2,7 @@
 // validation, normalisation of the global set, work planning and launches.
 // Nothing here allocates device memory or synchronises the host.
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -20,6 +21,11 @@ constexpr int kMaxN = SWA_MAX_N;
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool supported_d(int D) { return D == 64 || D == 128; }
+// The kernels mask a key by setting its raw score to -inf before the multiply
+// by scale * log2(e) and take the running max on raw scores: both need a
+// positive, finite multiplier.  (scale <= 0 has no meaning for a softmax
+// temperature; NaN fails the comparison.)
+bool valid_scale(float scale) { return scale > 0.f && std::isfinite(scale * kLog2e); }
 bool known_dtype(int dt) { return dt == SWA_F32 || dt == SWA_BF16; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -135,6 +141,37 @@ int run_decode(DecodeParams& p, void* out, float* lse, int D, int dtype, bool pa
     return combine_decode(p, out, lse, D, dtype, stream);
 }
 
+// Validates the arguments of a ring decode (with n_sink sink entries) and
+// fills its launch parameters, the split plan included; the caller supplies
+// the partials buffer.
+int plan_ring_decode(DecodeParams& p, const void* q, const void* kcache, const void* vcache,
+                     const int32_t* ring_head, const int32_t* cache_len, const void* ksink,
+                     const void* vsink, int n_sink, const void* out, int B, int Hq, int Hkv,
+                     int W, int D, float scale, int dtype) {
+    if (!q || !kcache || !vcache || !ring_head || !cache_len || !out) return SWA_ERR_ARG;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0 || D <= 0 || Hq % Hkv != 0) return SWA_ERR_ARG;
+    if (n_sink < 0 || n_sink > kMaxN || (n_sink > 0 && (!ksink || !vsink))) return SWA_ERR_ARG;
+    if (!valid_scale(scale)) return SWA_ERR_ARG;
+    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.kcache = kcache;
+    p.vcache = vcache;
+    p.ring_head = ring_head;
+    p.cache_len = cache_len;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.W = W;
+    p.group = Hq / Hkv;
+    p.scale_log2 = scale * kLog2e;
+    decode_splits(dtype, B, Hq, Hkv, W, &p.ring_splits, &p.slots_per_split);
+    p.ksink = ksink;
+    p.vsink = vsink;
+    p.n_sink = n_sink;
+    return SWA_OK;
+}
+
 // log2 of a power of two in [1, 2^20], else -1
 int page_shift_of(int P) {
     for (int sh = 0; sh <= 20; sh++)
@@ -177,6 +214,7 @@ int swa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, 
     if (Hq % Hkv != 0) return SWA_ERR_ARG;
     if (win_left < 0 || win_right < 0 || dilation < 1) return SWA_ERR_ARG;
     if (n_global < 0 || (n_global > 0 && !global_idx)) return SWA_ERR_ARG;
+    if (!valid_scale(scale)) return SWA_ERR_ARG;
     if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
 
     std::vector<int32_t> g;
@@ -271,6 +309,7 @@ int swa_fwd_cached(const void* q, const void* k, const void* v, const void* kcac
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || n <= 0 || n > kMaxN || W <= 0 || W > kMaxN || D <= 0)
         return SWA_ERR_ARG;
     if (Hq % Hkv != 0 || win_left < 0 || win_left > W) return SWA_ERR_ARG;
+    if (!valid_scale(scale)) return SWA_ERR_ARG;
     if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
 
     FwdParams p;
@@ -317,30 +356,13 @@ int swa_decode_sinks(const void* q, const void* kcache, const void* vcache,
                      const void* vsink, int n_sink, void* out, float* lse, int B, int Hq,
                      int Hkv, int W, int D, float scale, void* workspace,
                      size_t workspace_bytes, int dtype, hipStream_t stream) {
-    if (!q || !kcache || !vcache || !ring_head || !cache_len || !out) return SWA_ERR_ARG;
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || W <= 0 || D <= 0 || Hq % Hkv != 0) return SWA_ERR_ARG;
-    if (n_sink < 0 || n_sink > kMaxN || (n_sink > 0 && (!ksink || !vsink))) return SWA_ERR_ARG;
-    if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
+    DecodeParams p;
+    const int st = plan_ring_decode(p, q, kcache, vcache, ring_head, cache_len, ksink, vsink,
+                                    n_sink, out, B, Hq, Hkv, W, D, scale, dtype);
+    if (st != SWA_OK) return st;
     if (!workspace || workspace_bytes < swa_decode_sinks_workspace_size(B, Hq, W, D, n_sink))
         return SWA_ERR_WORKSPACE;
-    DecodeParams p;
-    std::memset(&p, 0, sizeof p);
-    p.q = q;
-    p.kcache = kcache;
-    p.vcache = vcache;
-    p.ring_head = ring_head;
-    p.cache_len = cache_len;
     p.partials = (float*)workspace;
-    p.B = B;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.W = W;
-    p.group = Hq / Hkv;
-    p.scale_log2 = scale * kLog2e;
-    decode_splits(dtype, B, Hq, Hkv, W, &p.ring_splits, &p.slots_per_split);
-    p.ksink = ksink;
-    p.vsink = vsink;
-    p.n_sink = n_sink;
     return run_decode(p, out, lse, D, dtype, false, stream);
 }
 
@@ -383,6 +405,7 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
         return SWA_ERR_ARG;
     const int sh = page_shift_of(page_size);
     if (sh < 0 || (int64_t)nb * page_size < (int64_t)W + page_size - 1) return SWA_ERR_ARG;
+    if (!valid_scale(scale)) return SWA_ERR_ARG;
     if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < swa_decode_workspace_size(B, Hq, W, D))
         return SWA_ERR_WORKSPACE;
@@ -438,6 +461,7 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
     if (Hq % Hkv != 0) return SWA_ERR_ARG;
     if (win_left < 0 || win_right < 0 || dilation < 1) return SWA_ERR_ARG;
     if (n_global < 0 || (n_global > 0 && !global_idx)) return SWA_ERR_ARG;
+    if (!valid_scale(scale)) return SWA_ERR_ARG;
     if (!supported_d(D) || !known_dtype(dtype)) return SWA_ERR_UNSUPPORTED;
     std::vector<int32_t> g;
     if (n_global > 0) {
@@ -541,3 +565,4 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
 }
 
 }  // extern "C"
+

@@ -14,8 +14,6 @@ namespace swa {
 constexpr int BN = 64;        // keys per K/V tile
 constexpr int kFarAway = -(1 << 30);  // residue coordinate outside every window
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 template <int D, int NW>
 struct TileCfg {
     static constexpr int NT = 64 * NW;                          // threads per workgroup

@@ -274,3 +274,99 @@ def test_bwd_validation(lib):
     assert call(N=1024, g=many, ng=300) == UNSUP                     # > 256 distinct
     assert call(g=(ctypes.c_int32 * 2)(0, 5), ng=2) == WS            # no room for them
     assert call(ws=None) == WS and call(wsb=need - 1) == WS
+
+
+BAD_SCALES = [0.0, -0.0, -0.125, float("nan"), float("inf"), float("-inf"), 3.0e38]
+
+
+@pytest.mark.parametrize("scale", BAD_SCALES)
+def test_scale_must_be_positive_and_finite(lib, scale):
+    """The kernels mask keys with -inf on the raw scores and take the running
+    max before multiplying by scale * log2(e), so every entry point that takes
+    a scale refuses one that is not positive and finite (3e38 * log2(e)
+    overflows float32).  The D = 80 calls show the order: a good scale passes
+    on to the head-dimension check (SWA_ERR_UNSUPPORTED), a bad one stops at
+    SWA_ERR_ARG before it."""
+    F = ctypes.c_float
+    assert fwd(lib, scale=scale) == ARG
+    assert fwd(lib, scale=scale, D=80) == ARG and fwd(lib, scale=0.1, D=80) == UNSUP
+    cached = lambda s, D: lib.swa_fwd_cached(P, P, P, P, P, P, P, P, None, 1, 8, 2, 64, 128,
+                                             D, 127, F(s), 1, None)
+    assert cached(scale, 128) == ARG and cached(scale, 80) == ARG and cached(0.1, 80) == UNSUP
+    need = lib.swa_decode_workspace_size(2, 8, 64, 128)
+    dec = lambda s, D: lib.swa_decode(P, P, P, P, P, P, None, 2, 8, 2, 64, D, F(s), P, need, 1,
+                                      None)
+    assert dec(scale, 128) == ARG and dec(scale, 80) == ARG and dec(0.1, 80) == UNSUP
+    sinks = lambda s, D: lib.swa_decode_sinks(P, P, P, P, P, P, P, 4, P, None, 2, 8, 2, 64, D,
+                                              F(s), P, 1 << 30, 1, None)
+    assert sinks(scale, 128) == ARG and sinks(0.1, 80) == UNSUP
+    need_p = lib.swa_decode_workspace_size(2, 8, 100, 128)
+    paged = lambda s, D: lib.swa_decode_paged(P, P, P, P, P, P, None, 2, 8, 2, 16, 16, 8, 100,
+                                              D, F(s), P, need_p, 1, None)
+    assert paged(scale, 128) == ARG and paged(0.1, 80) == UNSUP
+    need_b = lib.swa_bwd_workspace_size(1, 4, 2, 128, 128, 0)
+    bwd = lambda s, D: lib.swa_bwd(P, P, P, P, P, P, P, P, P, 1, 4, 2, 128, D, 7, 0, 1, None, 0,
+                                   F(s), 1, P, need_b, None)
+    assert bwd(scale, 128) == ARG and bwd(0.1, 80) == UNSUP
+
+
+def test_binding_checks_buffers_before_any_launch(lib):
+    """Caller-supplied buffers of the wrong shape or dtype, and inputs whose
+    dtypes disagree, raise SwaError naming the tensor before anything reaches
+    the C ABI (these are host tensors: the shape checks come before the device
+    check, which would otherwise be the error)."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros(1, 16, 4, 64, dtype=bf)
+    k = torch.zeros(1, 16, 2, 64, dtype=bf)
+
+    def raises(fn, name):
+        with pytest.raises(binding.SwaError) as e:
+            fn()
+        assert f"{name} must be" in str(e.value), str(e.value)
+
+    raises(lambda: binding.fwd(q, k, k, win_left=3, out=torch.zeros(1, 16, 4, 32, dtype=bf)),
+           "out")
+    raises(lambda: binding.fwd(q, k, k, win_left=3, out=torch.zeros(1, 16, 4, 64, dtype=f32)),
+           "out")
+    raises(lambda: binding.fwd(q, k, k, win_left=3, lse=torch.zeros(1, 4, 15)), "lse")
+    raises(lambda: binding.fwd(q, k, k.float(), win_left=3), "v")
+    # decode: an fp32 query over a bf16 ring would read past the ring
+    kc = torch.zeros(2, 2, 32, 64, dtype=bf)
+    qd = torch.zeros(2, 4, 64, dtype=bf)
+    head = torch.zeros(2, dtype=torch.int32)
+    raises(lambda: binding.decode(qd.float(), kc, kc, head, head), "kcache")
+    raises(lambda: binding.decode(qd, kc, kc, head.long(), head), "ring_head")
+    raises(lambda: binding.decode(qd, kc, kc, head, head[:1]), "cache_len")
+    raises(lambda: binding.decode(qd, kc, kc, head, head, out=torch.zeros(2, 4, 32, dtype=bf)),
+           "out")
+    raises(lambda: binding.decode(qd, kc, kc, head, head, lse=torch.zeros(2, 5)), "lse")
+    kn = torch.zeros(2, 2, 64, dtype=bf)
+    raises(lambda: binding.kv_append(kc, kc, kn.float(), kn, head, head), "k_new")
+    raises(lambda: binding.kv_append(kc, kc.float(), kn, kn, head, head), "vcache")
+    ks = torch.zeros(2, 2, 4, 64, dtype=bf)
+    raises(lambda: binding.decode_sinks(qd, kc, kc, head, head, ks, ks.float()), "vsink")
+    raises(lambda: binding.decode_sinks(qd, kc, kc, head, head, ks, ks,
+                                        out=torch.zeros(3, 4, 64, dtype=bf)), "out")
+    qc = torch.zeros(2, 8, 4, 64, dtype=bf)
+    kch = torch.zeros(2, 8, 2, 64, dtype=bf)
+    raises(lambda: binding.fwd_cached(qc, kch, kch, kc, kc, head, head, win_left=4,
+                                      lse=torch.zeros(2, 4, 9)), "lse")
+    pool = torch.zeros(8, 2, 16, 64, dtype=bf)
+    table = torch.zeros(2, 4, dtype=torch.int32)
+    raises(lambda: binding.decode_paged(qd, pool, pool, table, head, window=32,
+                                        out=torch.zeros(2, 4, 64, dtype=f32)), "out")
+    raises(lambda: binding.decode_paged(qd.float(), pool, pool, table, head, window=32),
+           "kpool")
+    raises(lambda: binding.kv_append_paged(pool, pool, kch, kch.float(), table, head, window=32),
+           "v")
+    out = torch.zeros_like(q)
+    lse = torch.zeros(1, 4, 16)
+    raises(lambda: binding.bwd(q, k, k, out, lse, out, win_left=3,
+                               dk=torch.zeros(1, 16, 4, 64, dtype=bf)), "dk")
+    raises(lambda: binding.bwd(q, k, k, out, lse, out, win_left=3,
+                               dq=torch.zeros(1, 16, 4, 64, dtype=f32)), "dq")
+    with pytest.raises(binding.SwaError, match="bwd shape mismatch"):
+        binding.bwd(q, k, k, out, lse[:, :, :8], out, win_left=3)
+    raises(lambda: binding.bwd(q, k, k, out, lse.double(), out, win_left=3), "lse")
+    raises(lambda: binding.bwd(q, k, k, out, lse, out.float(), win_left=3), "dout")
