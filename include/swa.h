@@ -234,6 +234,37 @@ int swa_decode(const void* q, const void* kcache, const void* vcache,
 size_t swa_decode_workspace_size(int B, int Hq, int W, int D);
 
 /*
+ * swa_decode_noalloc: swa_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus the
+ * workspace), same kernels and the same result bit for bit.  The split
+ * partials live in a device array inside the library,
+ * SWA_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on a GPU until
+ * the process ends; the call itself allocates nothing.
+ *
+ * Every call on one GPU shares that GPU's array: two calls that overlap in
+ * time on one GPU (different streams, or host threads) race and give wrong
+ * results; calls on one stream are ordered and safe.  The array needs no
+ * clearing (each call writes every record it reads).  `stream` must belong to
+ * the current device.
+ *
+ * A launch needs B * Hq * splits * (D + 4) * 4 bytes of it, where splits is
+ * the number of slot ranges each ring is cut into (the bf16 kernel with one
+ * range per ring, e.g. 64 sequences x 8 kv heads, needs none).  With the
+ * 16 MiB array, 64 sequences x 32 heads at D = 128 fit up to 15 ranges.
+ *
+ * Errors: as swa_decode, except SWA_ERR_WORKSPACE means the launch needs more
+ * than SWA_NOALLOC_SCRATCH_BYTES; SWA_ERR_HIP also if the array's device
+ * address cannot be found.
+ */
+#define SWA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int swa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                       const int32_t* ring_head, const int32_t* cache_len,
+                       void* out, float* lse,
+                       int B, int Hq, int Hkv, int W, int D, float scale,
+                       int dtype, hipStream_t stream);
+
+/*
  * swa_decode_sinks: swa_decode plus n_sink attention-sink entries that stay
  * visible to every step and are never evicted (mhpn.cn "Dilated sliding
  * window", section 3: the first tokens kept as attention-sink anchors; aiqz.cc,

@@ -66,6 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swa_bwd.restype = I
     lib.swa_bwd_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.swa_bwd_workspace_size.restype = SZ
+    lib.swa_decode_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.swa_decode_noalloc.restype = I
     lib.swa_decode_workspace_size.argtypes = [I, I, I, I]
     lib.swa_decode_workspace_size.restype = SZ
     lib.swa_status_string.argtypes = [I]
@@ -285,6 +287,36 @@ def decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                         _dtype_code(q), _stream(q))
     _check(st, "swa_decode")
+    return (out, lse) if return_lse else out
+
+
+def decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                   ring_head: torch.Tensor, cache_len: torch.Tensor, *,
+                   scale: float | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, return_lse: bool = True):
+    """decode() without a workspace: the library keeps the split partials in
+    its own per-GPU array (calls that overlap in time on one GPU race).  Pass
+    out (and lse) to allocate nothing at all."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, W = kcache.shape[1], kcache.shape[2]
+    if kcache.shape != (B, Hkv, W, D) or vcache.shape != kcache.shape:
+        raise SwaError(-1, "decode shape mismatch")
+    _same(q, kcache=kcache, vcache=vcache)
+    _ring_state(ring_head, cache_len, B, q)
+    _buffer(out, "out", q.shape, q.dtype, q)
+    _buffer(lse, "lse", (B, Hq), torch.float32, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.swa_decode_noalloc(_dev(q, "q"), _dev(kcache, "kcache"), _dev(vcache, "vcache"),
+                                _dev(ring_head, "ring_head"), _dev(cache_len, "cache_len"),
+                                _dev(out, "out"), _dev(lse, "lse"), B, Hq, Hkv, W, D,
+                                float(scale), _dtype_code(q), _stream(q))
+    _check(st, "swa_decode_noalloc")
     return (out, lse) if return_lse else out
 
 

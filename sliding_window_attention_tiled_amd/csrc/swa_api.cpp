@@ -5,7 +5,10 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
+
+#include <hip/hip_runtime.h>
 
 #include "swa_kernels.h"
 
@@ -566,3 +569,60 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
 
 }  // extern "C"
 
+// ---- allocation-free decode ---------------------------------------------------------
+// swa_decode_noalloc keeps its split partials in this file-scope device array
+// instead of a caller workspace.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: the device address is looked up with
+// hipGetSymbolAddress once per device, with that device current, and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SWA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// Device address of the current device's scratch (looked up on the first call
+// made on that device).
+int scratch_address(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SWA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SWA_ERR_HIP;
+        scratch_dev[dev] = p;
+    }
+    *ptr = scratch_dev[dev];
+    return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" int swa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                                  const int32_t* ring_head, const int32_t* cache_len, void* out,
+                                  float* lse, int B, int Hq, int Hkv, int W, int D, float scale,
+                                  int dtype, hipStream_t stream) {
+    DecodeParams p;
+    int st = plan_ring_decode(p, q, kcache, vcache, ring_head, cache_len, nullptr, nullptr, 0,
+                              out, B, Hq, Hkv, W, D, scale, dtype);
+    if (st != SWA_OK) return st;
+    // The partial records this launch writes: one per (sequence, query head,
+    // slot range); a bf16 launch with one range per ring writes out and lse
+    // directly and needs none.  Every record is written before the merge reads
+    // it, so nothing has to be cleared first.
+    if (!(dtype == SWA_BF16 && p.ring_splits == 1)) {
+        const size_t rec = (size_t)swa::partial_floats(D) * sizeof(float);
+        const size_t rows = (size_t)B * Hq;
+        if (rows > SWA_NOALLOC_SCRATCH_BYTES / rec / (size_t)p.ring_splits)
+            return SWA_ERR_WORKSPACE;
+    }
+    void* ptr = nullptr;
+    st = scratch_address(&ptr);
+    if (st != SWA_OK) return st;
+    p.partials = (float*)ptr;
+    return run_decode(p, out, lse, D, dtype, false, stream);
+}
