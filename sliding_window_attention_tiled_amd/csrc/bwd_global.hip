@@ -12,11 +12,13 @@
 // each with j <= i when causal.  Same chain rule as the band passes:
 // dS = P (dP - delta), dq = scale sum dS k, dk = scale sum dS q,
 // dv = sum P dout.  Four passes:
-//   rows_dq    dq of global rows over E_row, per key chunk, float32 atomics
+//   rows_dq    dq of global rows over E_row, one float32 partial per key chunk
 //   rows_dkdv  dk, dv of every key over E_row, read-modify-write
 //   cols_dq    dq of non-global rows over E_col, read-modify-write
-//   cols_dkdv  dk, dv of global keys over E_col, per row chunk, float32 atomics
-//   add_dq / add_dkdv fold the atomic accumulators into dq / dk, dv.
+//   cols_dkdv  dk, dv of global keys over E_col, one float32 partial per row chunk
+//   add_dq / add_dkdv sum the partials in chunk order into dq / dk, dv.
+// Every sum has a fixed order (no atomics), so the backward is bitwise
+// repeatable.
 // bf16 runs them on MFMA with the global tokens of a 16-wide block as the
 // columns of 16x16 tiles; float32 runs them on the vector ALUs, rows (or keys)
 // of a workgroup spread over lanes with tiles of 32 partners staged in LDS.
@@ -173,9 +175,11 @@ __global__ __launch_bounds__(NT) void rows_dq_kernel(const GlobalBwdParams g) {
         }
     }
     if (!row_ok) return;
-    float* out = g.dq_acc + (((size_t)b * g.Hq + hq) * g.n_global + gi) * D + part * DQ;
+    float* out = g.dq_part +
+                 ((((size_t)b * g.Hq + hq) * g.n_global + gi) * g.n_key_chunks + chunk) * D +
+                 part * DQ;
 #pragma unroll
-    for (int d = 0; d < DQ; d++) atomicAdd(out + d, acc[d]);
+    for (int d = 0; d < DQ; d++) out[d] = acc[d];
 }
 
 // ---- cols_dkdv: dk, dv of global keys over E_col -----------------------------
@@ -262,11 +266,13 @@ __global__ __launch_bounds__(NT) void cols_dkdv_kernel(const GlobalBwdParams g) 
         }
     }
     if (!key_ok) return;
-    float* out = g.dkv_acc + (((size_t)b * g.Hkv + kvh) * g.n_global + gk) * 2 * D + part * DQ;
+    float* out = g.dkv_part +
+                 ((((size_t)b * g.Hkv + kvh) * g.n_global + gk) * g.n_row_chunks + chunk) * 2 * D +
+                 part * DQ;
 #pragma unroll
     for (int d = 0; d < DQ; d++) {
-        atomicAdd(out + d, dk[d]);
-        atomicAdd(out + D + d, dv[d]);
+        out[d] = dk[d];
+        out[D + d] = dv[d];
     }
 }
 
@@ -487,12 +493,12 @@ __device__ __forceinline__ bool extra_pair_fast(const GlobalBwdParams& g, int i,
 // chunk); waves take 16-key blocks in turn.  S^T = K Q_G^T puts the global rows
 // in the columns, so dS^T is the A operand of dq_G = dS K; the wave stages its
 // K block in LDS for the transposed B operand.  The four waves' dq_G are summed
-// in LDS and added to the float32 accumulator with atomics.
+// in LDS in wave order and stored as the chunk's float32 partial.
 template <int D>
 __global__ __launch_bounds__(kMfmaNT) void rows_dq_mfma_kernel(const GlobalBwdParams g) {
     constexpr int KS = D / 32, DB = D / 16, P = D + 8;
     __shared__ __attribute__((aligned(16))) __bf16 kl[4][16 * P];
-    __shared__ float red[16 * D];
+    __shared__ float red[4][16 * D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l16 = lane & 15, grp = lane >> 4;
     int L = blockIdx.x;
@@ -503,7 +509,6 @@ __global__ __launch_bounds__(kMfmaNT) void rows_dq_mfma_kernel(const GlobalBwdPa
     const int hq = L % g.Hq;
     const int b = L / g.Hq;
     const int kvh = hq / g.group;
-    for (int i = threadIdx.x; i < 16 * D; i += kMfmaNT) red[i] = 0.f;
 
     const int gi = rt * 16 + l16;
     const bool gi_ok = gi < g.n_global;
@@ -570,17 +575,17 @@ __global__ __launch_bounds__(kMfmaNT) void rows_dq_mfma_kernel(const GlobalBwdPa
 #pragma unroll
         for (int d = 0; d < DB; d++) acc[d] = mma_k16(dsa, tr_block<P>(kw, grp, l16, d), acc[d]);
     }
-    __syncthreads();
     // acc[d][e]: global row rt*16 + 4 grp + e, dimension 16 d + l16
 #pragma unroll
     for (int d = 0; d < DB; d++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) atomicAdd(&red[(grp * 4 + e) * D + d * 16 + l16], acc[d][e]);
+        for (int e = 0; e < 4; e++) red[wave][(grp * 4 + e) * D + d * 16 + l16] = acc[d][e];
     __syncthreads();
     for (int i = threadIdx.x; i < 16 * D; i += kMfmaNT) {
         const int r = rt * 16 + i / D;
         if (r < g.n_global)
-            atomicAdd(g.dq_acc + (((size_t)b * g.Hq + hq) * g.n_global + r) * D + i % D, red[i]);
+            g.dq_part[((((size_t)b * g.Hq + hq) * g.n_global + r) * g.n_key_chunks + chunk) * D +
+                      i % D] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
     }
 }
 
@@ -776,13 +781,14 @@ __global__ __launch_bounds__(kMfmaNT) void cols_dq_mfma_kernel(const GlobalBwdPa
 // the group.  S = Q K_G^T puts the global keys in the columns, so dS^T and P^T
 // are the A operands of dk_G = dS^T Q and dv_G = P^T dout; the wave stages its
 // Q and dout blocks in LDS for the transposed B operands.  The four waves'
-// sums meet in LDS and go to the float32 accumulator with atomics.
+// sums are added in LDS in wave order and stored as the chunk's float32
+// partial.
 template <int D>
 __global__ __launch_bounds__(kMfmaNT) void cols_dkdv_mfma_kernel(const GlobalBwdParams g) {
     constexpr int KS = D / 32, DB = D / 16, P = D + 8;
     __shared__ __attribute__((aligned(16))) __bf16 qw[4][16 * P];
     __shared__ __attribute__((aligned(16))) __bf16 ow[4][16 * P];
-    __shared__ float red[16 * 2 * D];
+    __shared__ float red[4][16 * 2 * D];
     __shared__ int gp[SWA_MAX_GLOBAL];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, grp = lane >> 4;
@@ -794,7 +800,6 @@ __global__ __launch_bounds__(kMfmaNT) void cols_dkdv_mfma_kernel(const GlobalBwd
     const int kvh = L % g.Hkv;
     const int b = L / g.Hkv;
     for (int i = tid; i < g.n_global; i += kMfmaNT) gp[i] = g.gpos[i];
-    for (int i = tid; i < 16 * 2 * D; i += kMfmaNT) red[i] = 0.f;
     __syncthreads();
     const int gk = kt * 16 + l16;
     const bool gk_ok = gk < g.n_global;
@@ -886,25 +891,22 @@ __global__ __launch_bounds__(kMfmaNT) void cols_dkdv_mfma_kernel(const GlobalBwd
     for (int d = 0; d < DB; d++)
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            atomicAdd(&red[(grp * 4 + e) * 2 * D + d * 16 + l16], dkg[d][e]);
-            atomicAdd(&red[(grp * 4 + e) * 2 * D + D + d * 16 + l16], dvg[d][e]);
+            red[wave][(grp * 4 + e) * 2 * D + d * 16 + l16] = dkg[d][e];
+            red[wave][(grp * 4 + e) * 2 * D + D + d * 16 + l16] = dvg[d][e];
         }
     __syncthreads();
     for (int i = tid; i < 16 * 2 * D; i += kMfmaNT) {
         const int r = kt * 16 + i / (2 * D);
         if (r < g.n_global)
-            atomicAdd(g.dkv_acc + (((size_t)b * g.Hkv + kvh) * g.n_global + r) * 2 * D + i % (2 * D),
-                      red[i]);
+            g.dkv_part[((((size_t)b * g.Hkv + kvh) * g.n_global + r) * g.n_row_chunks + chunk) *
+                           2 * D +
+                       i % (2 * D)] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
     }
 }
 
-// ---- accumulators ------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void zero_kernel(float* p, size_t n) {
-    const size_t i = (size_t)blockIdx.x * NT + threadIdx.x;
-    if (i < n) p[i] = 0.f;
-}
-
-// dq of global rows += scale * dq_acc; one thread per element
+// ---- partials ----------------------------------------------------------------------
+// dq of global rows += scale * (sum of the key chunks' partials, in chunk
+// order); one thread per element
 template <int D, typename T>
 __global__ __launch_bounds__(NT) void add_dq_kernel(const GlobalBwdParams g) {
     const size_t e = (size_t)blockIdx.x * NT + threadIdx.x;
@@ -916,11 +918,15 @@ __global__ __launch_bounds__(NT) void add_dq_kernel(const GlobalBwdParams g) {
     r /= g.n_global;
     const int hq = (int)(r % g.Hq);
     const int b = (int)(r / g.Hq);
+    const float* part = g.dq_part + (e / D) * g.n_key_chunks * D + d;
+    float sum = 0.f;
+    for (int c = 0; c < g.n_key_chunks; c++) sum += part[(size_t)c * D];
     T* p = (T*)g.dq + (((size_t)b * g.N + g.gpos[gi]) * g.Hq + hq) * D + d;
-    *p = (T)((float)*p + g.scale * g.dq_acc[e]);
+    *p = (T)((float)*p + g.scale * sum);
 }
 
-// dk, dv of global keys += (scale * dk_acc, dv_acc); one thread per element
+// dk, dv of global keys += (scale * dk, dv summed over the row chunks'
+// partials in chunk order); one thread per element
 template <int D, typename T>
 __global__ __launch_bounds__(NT) void add_dkdv_kernel(const GlobalBwdParams g) {
     const size_t e = (size_t)blockIdx.x * NT + threadIdx.x;
@@ -932,12 +938,17 @@ __global__ __launch_bounds__(NT) void add_dkdv_kernel(const GlobalBwdParams g) {
     r /= g.n_global;
     const int kvh = (int)(r % g.Hkv);
     const int b = (int)(r / g.Hkv);
-    const float* acc = g.dkv_acc + (((size_t)b * g.Hkv + kvh) * g.n_global + gk) * 2 * D;
+    const float* part = g.dkv_part + (e / D) * g.n_row_chunks * 2 * D;
+    float sk = 0.f, sv = 0.f;
+    for (int c = 0; c < g.n_row_chunks; c++) {
+        sk += part[(size_t)c * 2 * D + d];
+        sv += part[(size_t)c * 2 * D + D + d];
+    }
     const size_t o = (((size_t)b * g.N + g.gpos[gk]) * g.Hkv + kvh) * D + d;
     T* kp = (T*)g.dk + o;
     T* vp = (T*)g.dv + o;
-    *kp = (T)((float)*kp + g.scale * acc[d]);
-    *vp = (T)((float)*vp + acc[D + d]);
+    *kp = (T)((float)*kp + g.scale * sk);
+    *vp = (T)((float)*vp + sv);
 }
 
 unsigned blocks_for(size_t n) { return (unsigned)((n + NT - 1) / NT); }
@@ -946,8 +957,6 @@ template <int D, typename T>
 hipError_t launch_all(const GlobalBwdParams& g, hipStream_t s) {
     const size_t nq = (size_t)g.B * g.Hq * g.n_global * D;
     const size_t nkv = (size_t)g.B * g.Hkv * g.n_global * 2 * D;
-    hipLaunchKernelGGL(zero_kernel, dim3(blocks_for(nq)), dim3(NT), 0, s, g.dq_acc, nq);
-    hipLaunchKernelGGL(zero_kernel, dim3(blocks_for(nkv)), dim3(NT), 0, s, g.dkv_acc, nkv);
     const dim3 rows_dq_grid(g.B * g.Hq * g.row_tiles * g.n_key_chunks);
     const dim3 cols_dkdv_grid(g.B * g.Hkv * g.key_tiles * g.n_row_chunks);
     const dim3 cols_dq_grid(g.B * g.Hq * g.n_row_tiles_all);

@@ -434,13 +434,31 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
 }
 
 // Workspace of swa_bwd: per-row dout . out, then (global tokens only) the
-// float32 accumulators of the global rows' dq and the global keys' dk, dv.
+// float32 partial sums of the global rows' dq (one per key chunk) and of the
+// global keys' dk, dv (one per row chunk).
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static size_t bwd_delta_bytes(int B, int Hq, int N) {
     return align256((size_t)B * Hq * N * sizeof(float));
 }
-static size_t bwd_dq_acc_bytes(int B, int Hq, int ng, int D) {
-    return align256((size_t)B * Hq * ng * D * sizeof(float));
+
+// Splits of the N keys (or rows) of the global tokens' passes: about 512
+// workgroups per pass for a 16-token block, each split a multiple of 32 keys.
+// Independent of the number of global tokens, so that the workspace grows
+// with it.
+static void bwd_global_chunks(int B, int H, int N, int* chunk, int* nchunks) {
+    const int64_t nc = std::min<int64_t>(cdiv(N, 256), std::max<int64_t>(1, cdiv(512, (int64_t)B * H)));
+    *chunk = (int)(cdiv(cdiv(N, nc), 32) * 32);
+    *nchunks = (int)cdiv(N, *chunk);
+}
+static size_t bwd_dq_part_bytes(int B, int Hq, int N, int ng, int D) {
+    int ck, nc;
+    bwd_global_chunks(B, Hq, N, &ck, &nc);
+    return align256((size_t)B * Hq * ng * nc * D * sizeof(float));
+}
+static size_t bwd_dkv_part_bytes(int B, int Hkv, int N, int ng, int D) {
+    int ck, nc;
+    bwd_global_chunks(B, Hkv, N, &ck, &nc);
+    return align256((size_t)B * Hkv * ng * nc * 2 * D * sizeof(float));
 }
 
 size_t swa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int n_global) {
@@ -448,9 +466,7 @@ size_t swa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int D, int n_global
     if (n_global < 0) return 0;
     const int ng = std::min(n_global, std::min(N, SWA_MAX_GLOBAL));
     size_t bytes = bwd_delta_bytes(B, Hq, N);
-    if (ng > 0)
-        bytes += bwd_dq_acc_bytes(B, Hq, ng, D) +
-                 align256((size_t)B * Hkv * ng * 2 * D * sizeof(float));
+    if (ng > 0) bytes += bwd_dq_part_bytes(B, Hq, N, ng, D) + bwd_dkv_part_bytes(B, Hkv, N, ng, D);
     return bytes;
 }
 
@@ -526,8 +542,8 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         gb.dk = dk;
         gb.dv = dv;
         char* ws = (char*)workspace + bwd_delta_bytes(B, Hq, N);
-        gb.dq_acc = (float*)ws;
-        gb.dkv_acc = (float*)(ws + bwd_dq_acc_bytes(B, Hq, ng, D));
+        gb.dq_part = (float*)ws;
+        gb.dkv_part = (float*)(ws + bwd_dq_part_bytes(B, Hq, N, ng, D));
         gb.B = B;
         gb.Hq = Hq;
         gb.Hkv = Hkv;
@@ -542,17 +558,10 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         gb.n_global = ng;
         for (int i = 0; i < ng; i++) gb.gpos[i] = g[i];
         gb.row_tiles = gb.key_tiles = (int)cdiv(ng, swa::kGlobalBwdItems);
-        // splits of the N keys (rows) so that each pass has about 512 workgroups:
-        // each split ends in float atomics of its 16 x D sums, so fewer,
-        // longer splits beat more parallelism here
-        const int64_t nkc = std::min<int64_t>(
-            cdiv(N, 256), std::max<int64_t>(1, cdiv(512, (int64_t)B * Hq * gb.row_tiles)));
-        gb.key_chunk = (int)(cdiv(cdiv(N, nkc), 32) * 32);
-        gb.n_key_chunks = (int)cdiv(N, gb.key_chunk);
-        const int64_t nrc = std::min<int64_t>(
-            cdiv(N, 256), std::max<int64_t>(1, cdiv(512, (int64_t)B * Hkv * gb.key_tiles)));
-        gb.row_chunk = (int)(cdiv(cdiv(N, nrc), 32) * 32);
-        gb.n_row_chunks = (int)cdiv(N, gb.row_chunk);
+        // splits of the N keys (rows): each split leaves a float32 partial
+        // that the add kernels sum in split order
+        bwd_global_chunks(B, Hq, N, &gb.key_chunk, &gb.n_key_chunks);
+        bwd_global_chunks(B, Hkv, N, &gb.row_chunk, &gb.n_row_chunks);
         gb.n_row_tiles_all = gb.n_key_tiles_all = (int)cdiv(N, 64);
         if ((int64_t)B * Hq * gb.n_row_tiles_all > INT32_MAX ||
             (int64_t)B * Hq * gb.row_tiles * gb.n_key_chunks > INT32_MAX ||

@@ -93,8 +93,8 @@ struct GlobalBwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* dq_acc;       // [B][Hq][n_global][D] float32, cleared by the launch
-    float* dkv_acc;      // [B][Hkv][n_global][2][D] float32, cleared by the launch
+    float* dq_part;      // [B][Hq][n_global][n_key_chunks][D] float32 partials
+    float* dkv_part;     // [B][Hkv][n_global][n_row_chunks][2][D] float32 partials
     int B, Hq, Hkv, N, group;
     int wl, wr, dil, causal;
     float scale, scale_log2;

@@ -170,3 +170,41 @@ def test_bwd_full_size_dilated_sampled(d):
     gk, gv = to_host_f64(dk), to_host_f64(dv)
     _check_grad(np.stack([gk[b, j, h] for b, h, j in sel]), rk, dt, f"d={d} sampled dk")
     _check_grad(np.stack([gv[b, j, h] for b, h, j in sel]), rv, dt, f"d={d} sampled dv")
+
+
+REPEAT_CASES = [
+    # name, B, Hq, Hkv, N, D, dtype, wl, wr, global positions
+    ("rep_bidir_globals_d64", 2, 6, 6, 2048, 64, "bf16", 128, 128, list(range(0, 2048, 256))),
+    ("rep_causal_gqa4_d128", 1, 8, 2, 1500, 128, "bf16", 300, 0, [0, 1, 700, 1499]),
+    ("rep_many_globals_d64", 1, 4, 2, 1200, 64, "bf16", 32, 32, list(range(3, 1200, 37))),
+    ("rep_f32_bidir", 1, 4, 4, 700, 64, "f32", 50, 50, [0, 350, 699]),
+]
+
+
+@pytest.mark.parametrize("case", REPEAT_CASES, ids=[c[0] for c in REPEAT_CASES])
+def test_bwd_with_globals_is_bitwise_repeatable(case):
+    """Every sum of the backward, those over the global tokens' split partials
+    included, has a fixed order: repeated calls give the same bits (and match
+    the oracle)."""
+    name, B, Hq, Hkv, N, D, dt, wl, wr, G = case
+    q, k, v = fwd_inputs(95, B, Hq, Hkv, N, D, dt)
+    g = fwd_inputs(96, B, Hq, Hkv, N, D, dt)[0]
+    log(f"[bwd repeat] {name}")
+    qd, kd, vd, gd = to_dev(q), to_dev(k), to_dev(v), to_dev(g)
+    kw = dict(win_left=wl, win_right=wr, global_idx=G)
+    out, lse = binding.fwd(qd, kd, vd, **kw)
+    first = None
+    for rep in range(3):
+        grads = binding.bwd(qd, kd, vd, out, lse, gd, **kw)
+        torch.cuda.synchronize()
+        bits_now = [t.view(torch.int16 if dt == "bf16" else torch.int32).cpu().clone()
+                    for t in grads]
+        if first is None:
+            first = bits_now
+        else:
+            for a, b_, nm in zip(first, bits_now, ("dq", "dk", "dv")):
+                assert torch.equal(a, b_), f"{name}: {nm} differs on call {rep + 1}"
+    rq, rk, rv = oracle.bwd(q, k, v, g, **kw)
+    _check_grad(to_host_f64(grads[0]), rq, dt, f"{name} dq")
+    _check_grad(to_host_f64(grads[1]), rk, dt, f"{name} dk")
+    _check_grad(to_host_f64(grads[2]), rv, dt, f"{name} dv")
