@@ -46,11 +46,13 @@ namespace {
 
 constexpr int kQB = 1;  // 32-query blocks per wave
 
-// GROWS = false: band workgroups (plus global key columns).
+// GROWS = false: band workgroups, with gathered tiles of the global keys
+//                after the band when GLOB.
 // GROWS = true : global query rows over one key chunk, partial output.
-template <int D, int QB, int NW, bool GROWS>
+template <int D, int QB, int NW, bool GROWS, bool GLOB>
 __global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1)
 void swa_fwd_bf16_kernel(const FwdParams p) {
+    constexpr bool kGathered = GLOB && !GROWS;
     using T = TileCfg<D, NW>;
     constexpr int KC = D / 16;   // 16-deep k-steps of QK^T
     constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -131,7 +133,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     // ---- prologue: tile 0 into stage 0 ---------------------------------------
     // (tile 0 is a band tile: the barrier below publishes gpos_lds before the
     // first gathered-key tile is loaded)
-    if (!GROWS)
+    if (kGathered)
         for (int i = threadIdx.x; i < p.n_global; i += T::NT) gpos_lds[i] = p.gpos[i];
     // With p.rotate the band tiles are walked in a rotated order: step j
     // takes the band tile whose absolute index (k_lo / BN + tile) is j modulo
@@ -160,15 +162,45 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     }
     __syncthreads();
 
+    // Without dilation the global keys a band row must not see again form
+    // index ranges of the sorted global list (published in gpos_lds by the
+    // barrier above): those inside the row's window, [g_in0, g_in1), and
+    // (causal) those after the row, from g_end on.  Entry gi of a gathered
+    // tile is visible to the row exactly when gi < g_in0 or g_in1 <= gi <
+    // g_end, so the tile's masks need two compares per element.
+    int g_in0[QB], g_in1[QB], g_end[QB];
+    const bool g_ranges = kGathered && ks.dil == 1;
+    if (g_ranges) {
+        // first entry >= x; the same number of steps on every lane
+        auto lower = [&](int x) {
+            int pos = 0;
+            for (int step = 1 << (31 - __builtin_clz(p.n_global)); step > 0; step >>= 1)
+                if (pos + step <= p.n_global && gpos_lds[pos + step - 1] < x) pos += step;
+            return pos;
+        };
+#pragma unroll
+        for (int qb = 0; qb < QB; qb++) {
+            const int i = qres[qb];   // the position (d = 1, r = 0)
+            g_in0[qb] = lower(i - p.wl);
+            g_in1[qb] = lower(i + p.wr + 1);
+            g_end[qb] = p.causal ? lower(i + 1) : p.n_global;
+        }
+    }
+
     for (int j = 0; j < ks.n_tiles; j++) {
         const int st = j & 1;
         const bool has_next = j + 1 < ks.n_tiles;
 
+
         // classify this tile for this wave (wave-uniform)
         const int jt = tile_at(j);
-        const bool band_tile = GROWS || jt < ks.n_band_tiles;
+        const bool band_tile = GROWS || !kGathered || jt < ks.n_band_tiles;
         const int kt0 = ks.k_lo + jt * BN;
         bool skip = false, need_mask = true;
+        // a gathered tile with at most 32 entries: its second 32-key block is
+        // padding, skipped
+        const int gi0 = (jt - ks.n_band_tiles) * BN;   // list index of a gathered tile's key 0
+        const bool half_tile = kGathered && !band_tile && p.n_global - gi0 <= 32;
         if (!GROWS && band_tile) {
             const int kt1 = kt0 + BN - 1;
             skip = w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl;
@@ -189,6 +221,20 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             // that LDS latency overlaps the matrix work (batches of 8 at D = 128
             // were 2.5% faster than 16: fewer registers held by fragments)
             constexpr int KBATCH = 2 * KC < 8 ? 2 * KC : 8;
+            if (half_tile) {
+#pragma unroll
+                for (int qb = 0; qb < QB; qb++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) s[qb][1][e] = -INFINITY;
+#pragma unroll
+                for (int kc = 0; kc < KC; kc++) {
+                    const bf16x8 a = *(const bf16x8*)(Ks + l32 * T::KP + kc * 16 + half * 8);
+#pragma unroll
+                    for (int qb = 0; qb < QB; qb++)
+                        s[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][kc],
+                                                                           s[qb][0], 0, 0, 0);
+                }
+            } else
 #pragma unroll
             for (int k0 = 0; k0 < KC; k0 += KBATCH / 2) {
                 bf16x8 a[KBATCH];
@@ -255,6 +301,23 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                                 if ((unsigned)(ko - lo) > span) s[qb][kb][e] = -INFINITY;
                             }
                     }
+                } else if (g_ranges) {
+                    // gathered global keys, d = 1: the index ranges above
+#pragma unroll
+                    for (int qb = 0; qb < QB; qb++) {
+                        const unsigned tail = (unsigned)(g_end[qb] - g_in1[qb]);
+#pragma unroll
+                        for (int kb = 0; kb < 2; kb++) {
+                            if (kb == 1 && half_tile) break;
+#pragma unroll
+                            for (int e = 0; e < 16; e++) {
+                                const int gi = gi0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+                                const bool vis = gi < g_in0[qb] ||
+                                                 (unsigned)(gi - g_in1[qb]) < tail;
+                                if (!vis) s[qb][kb][e] = -INFINITY;
+                            }
+                        }
+                    }
                 } else {
                     // gathered global keys: visible unless already in the band,
                     // and (causal) not after the query
@@ -318,6 +381,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             const int col_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
             for (int t = 0; t < 4; t++) {
+                if (t >= 2 && half_tile) break;   // keys 32..63: padding, weight 0
                 // V^T fragments of this step first: their LDS latency overlaps the
                 // exponentials below
                 bf16x8 va[DB];
@@ -410,13 +474,18 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
 
 template <int D, int QB, int NW>
 hipError_t launch_d(const FwdParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, false>), dim3(p.n_blocks), dim3(64 * NW),
-                       0, s, p);
+    if (p.n_global == 0) {
+        hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, false, false>), dim3(p.n_blocks),
+                           dim3(64 * NW), 0, s, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, false, true>), dim3(p.n_blocks),
+                       dim3(64 * NW), 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.n_global == 0) return e;
+    if (e != hipSuccess) return e;
     const int grid = p.B * p.Hkv * p.head_groups * p.g_rowgroups * p.g_nchunks;
-    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, true>), dim3(grid), dim3(64 * NW), 0, s,
-                       p);
+    hipLaunchKernelGGL((swa_fwd_bf16_kernel<D, QB, NW, true, false>), dim3(grid), dim3(64 * NW),
+                       0, s, p);
     return hipGetLastError();
 }
 
