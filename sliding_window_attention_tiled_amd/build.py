@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libswa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["swa_api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip",
+SOURCES = ["swa_api.cpp", "fwd_bf16.hip", "fwd_pp.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip",
            "bwd_f32.hip", "bwd_global.hip"]
 
 # Packed FP32 instructions stay off: every float operation is scalar per lane.

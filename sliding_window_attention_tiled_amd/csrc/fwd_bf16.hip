@@ -515,6 +515,7 @@ hipError_t launch_fwd_bf16(const FwdParams& band, int D, hipStream_t s) {
     constexpr double kL2Bytes = 4.0 * 1024 * 1024;
     const double reuse = (double)(p.bmq / BN) * (32 * (w8 ? 1 : 2)) * ((double)BN * D * 2 * 2);
     p.rotate = reuse >= kL2Bytes;
+    if (fwd_pp_applies(p, D)) return launch_fwd_pp(p, s);
     if (D == 128) return w8 ? launch_d<128, kQB, 8>(p, s) : launch_d<128, kQB, 4>(p, s);
     return w8 ? launch_d<64, kQB, 8>(p, s) : launch_d<64, kQB, 4>(p, s);
 }

@@ -160,6 +160,11 @@ FwdShape fwd_f32_shape(int group);
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_fwd_bf16(const FwdParams& p, int D, hipStream_t s);
+// Two-group (phase-offset) bf16 forward: D = 128, four query heads per
+// workgroup, band only (no global tokens, no ring).  launch_fwd_bf16 uses it
+// where it applies.
+bool fwd_pp_applies(const FwdParams& p, int D);
+hipError_t launch_fwd_pp(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, int D, hipStream_t s);
 FwdShape bwd_bf16_dq_shape(int group);
 int bwd_bf16_dkdv_keys();

@@ -39,6 +39,10 @@ SMALL = [
     ("n1", 1, 4, 4, 1, 128, "bf16", 5, 0, 1, None, None),
     ("n2_bidir_global", 2, 2, 1, 2, 64, "bf16", 5, 5, 1, [1], None),
     ("gqa8", 1, 16, 2, 300, 128, "bf16", 50, 0, 1, None, None),
+    ("bidir_dilated2_gqa4", 1, 8, 2, 1100, 128, "bf16", 70, 45, 2, None, None),
+    ("window_ge_n_gqa4", 2, 4, 1, 300, 128, "bf16", 1000, 1000, 1, None, None),
+    ("n3_causal_gqa4", 1, 4, 1, 3, 128, "bf16", 8, 0, 1, None, None),
+    ("zero_window_gqa4", 1, 8, 2, 200, 128, "bf16", 0, 0, 1, None, None),
     ("gqa3", 1, 6, 2, 300, 64, "bf16", 50, 10, 1, None, None),
     ("many_globals_256", 1, 2, 2, 2048, 64, "bf16", 16, 16, 1, list(range(0, 2048, 8)), None),
     ("dilation_gt_n", 1, 2, 2, 100, 64, "bf16", 3, 3, 150, [7], None),
@@ -136,6 +140,8 @@ def test_fwd_full_dilated_stack(dil):
 PROBES = [
     # name, N, Hq, Hkv, D, win_left, win_right, dilation, globals
     ("causal", 700, 2, 1, 128, 100, 0, 1, None),
+    ("causal_gqa4", 700, 4, 1, 128, 100, 0, 1, None),
+    ("dilated2_bidir_gqa4", 650, 4, 1, 128, 30, 17, 2, None),
     ("bidir_globals", 600, 1, 1, 64, 40, 40, 1, [0, 300, 599]),
     ("dilated3_globals", 650, 1, 1, 128, 30, 10, 3, [5, 400]),
     ("dilated8_causal_sink", 513, 4, 1, 128, 20, 0, 8, [0]),
