@@ -39,11 +39,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
 FWD_SOURCES = ["sliding_window_attention_tiled_amd/csrc/fwd_bf16.hip",
+               "sliding_window_attention_tiled_amd/csrc/fwd_pp.hip",
                "sliding_window_attention_tiled_amd/csrc/tile_common.h",
                "sliding_window_attention_tiled_amd/csrc/fwd_common.h",
                "sliding_window_attention_tiled_amd/csrc/device_common.h",
                "sliding_window_attention_tiled_amd/csrc/swa_kernels.h"]
-FWD_PROFILE = "profiles/swa_fwd_bf16_mistral_causal_w4096.md"
+FWD_PROFILE = "profiles/swa_fwd_pp_mistral_causal_w4096.md"
 
 
 def measured_traffic():
