@@ -383,11 +383,14 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
  *                        window attention: Mistral", section "global attention
  *                        tokens").  The pairs outside the band are summed in
  *                        float32 and added to the band's dq, dk, dv (one more
- *                        rounding of those rows in bf16).
+ *                        rounding of those rows in bf16).  Work split over
+ *                        key or row chunks writes one float32 partial per
+ *                        chunk, summed in chunk order: no atomics, and the
+ *                        same call gives the same bits every time.
  *   workspace            device scratch of swa_bwd_workspace_size() bytes
- *                        (per-row dout . out; with global tokens also float32
- *                        accumulators of their rows and keys); two calls in
- *                        flight at once must not share it
+ *                        (per-row dout . out; with global tokens also the
+ *                        float32 partials of their rows and keys); two calls
+ *                        in flight at once must not share it
  *
  * Errors: as swa_fwd (with lse, dout, dq, dk, dv required), plus
  * SWA_ERR_WORKSPACE for a missing or short workspace.
