@@ -54,7 +54,36 @@ def build() -> str:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_host_asan(objs)
     return LIB
+
+
+# AddressSanitizer on the host code only (the validator and planner in
+# swa_api.cpp): the sanitizer applies to the host side of that one file, the
+# kernels are the release objects.  The library expects the ASan runtime to be
+# preloaded into the process that loads it (tests/test_host_asan.py does).
+HOST_ASAN_LIB = os.path.join(PKG, "libswa_hostasan.so")
+HOST_ASAN_FLAGS = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+
+
+def build_host_asan(objs=None) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    if objs is None:
+        objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    api_obj = os.path.join(OBJ, "swa_api_hostasan.o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *HOST_ASAN_FLAGS, "-x", "hip", "-c",
+           os.path.join(CSRC, "swa_api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on swa_api.cpp (host ASan)")
+    others = [o for o in objs if not o.endswith(os.sep + "swa_api.o")]
+    tmp = HOST_ASAN_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_ASAN_FLAGS, api_obj,
+           *others, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, HOST_ASAN_LIB)
+    return HOST_ASAN_LIB
 
 
 if __name__ == "__main__":
