@@ -413,6 +413,23 @@ const char* swa_status_string(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int swa_version(void);
 
+/* Index-contract checks of the debug build (libswa_debug.so, compiled with
+ * SWA_DEBUG; not an operation of the method).  In that build the kernels check
+ * every global row they read or write against its tensor, ring slots and
+ * sink entries against the cache, LDS tile offsets against the tile, and the
+ * device-side state they are handed (ring_head, cache_len, seq_len, block_table
+ * entries) against its documented range before clamping it; a failed check is
+ * counted, once per thread that evaluates it, and never faults.  That build
+ * also adds workgroup barriers that run overlapped phases one after another
+ * and waits on every tile copy as soon as it is issued: its results match the
+ * release build's bit for bit unless a wait or barrier is missing there.
+ * This call waits for all work on the current device (hipDeviceSynchronize),
+ * stores the number of failed checks counted on that device since the last
+ * reset in *count (if count is non-null), and clears the counters when reset
+ * is non-zero.  Returns SWA_OK, SWA_ERR_HIP if a HIP call fails, and
+ * SWA_ERR_UNSUPPORTED in the release build (count is left unchanged). */
+int swa_debug_violations(unsigned long long* count, int reset);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,7 @@ library has not been built, the first call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -15,6 +16,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libswa.so")
+DEBUG_LIB_PATH = os.path.join(_PKG, "libswa_debug.so")
 
 SWA_F32, SWA_BF16 = 0, 1
 _STATUS = {0: "SWA_OK", -1: "SWA_ERR_ARG", -2: "SWA_ERR_UNSUPPORTED",
@@ -32,8 +34,35 @@ class SwaError(RuntimeError):
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libswa.so (once).  Raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = _open(path)
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route this module's calls through another build of the library with the
+    same C ABI (libswa_debug.so, say) inside the `with` block."""
+    global _lib
+    saved = _lib
+    _lib = _open(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def debug_violations(reset: bool = True) -> int:
+    """Failed index checks counted by the debug build's kernels on the current
+    device since the last reset (waits for the device).  Raises SwaError
+    (SWA_ERR_UNSUPPORTED) in the release build."""
+    n = ctypes.c_ulonglong(0)
+    _check(load_library().swa_debug_violations(ctypes.byref(n), int(reset)),
+           "swa_debug_violations")
+    return int(n.value)
+
+
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise SwaError(-4, f"{path} is missing: build it first "
                            "(python -m sliding_window_attention_tiled_amd.build)")
@@ -74,7 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swa_status_string.restype = ctypes.c_char_p
     lib.swa_version.argtypes = []
     lib.swa_version.restype = I
-    _lib = lib
+    lib.swa_debug_violations.argtypes = [ctypes.POINTER(ctypes.c_ulonglong), I]
+    lib.swa_debug_violations.restype = I
     return lib
 
 

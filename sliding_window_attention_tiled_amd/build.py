@@ -2,8 +2,10 @@
 
     python -m sliding_window_attention_tiled_amd.build
 
-Every call recompiles.  The objects go to csrc/_build/ and the library to the
-package directory, where binding.py loads it.
+Every call recompiles.  The objects go to csrc/_build/ and the libraries to
+the package directory, where binding.py loads them: libswa.so (release),
+libswa_debug.so (SWA_DEBUG checks) and libswa_hostasan.so (host code under
+AddressSanitizer).
 """
 from __future__ import annotations
 
@@ -32,13 +34,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-I", os.path.join(PKG, "..", "include")]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, objdir: str = OBJ, defines=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     extra = SOURCE_FLAGS.get(src, [])
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
-    if src.endswith(".cpp"):
-        cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o",
-               obj]
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *extra, *defines, *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -46,16 +47,38 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, lib: str, extra=()) -> str:
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib)
+    return lib
+
+
 def build() -> str:
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    _link(objs, LIB)
     build_host_asan(objs)
+    build_debug()
     return LIB
+
+
+# The debug build: every source compiled with SWA_DEBUG, which turns on the
+# kernels' index-contract counters (read with swa_debug_violations) and the
+# extra barriers and immediate copy waits that serialise overlapped phases.
+# Same C ABI as libswa.so; tests load it beside the release library and
+# compare the two bit for bit.
+DEBUG_LIB = os.path.join(PKG, "libswa_debug.so")
+DEBUG_OBJ = os.path.join(OBJ, "debug")
+
+
+def build_debug() -> str:
+    os.makedirs(DEBUG_OBJ, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, DEBUG_OBJ, ["-DSWA_DEBUG"]), SOURCES))
+    return _link(objs, DEBUG_LIB)
 
 
 # AddressSanitizer on the host code only (the validator and planner in
@@ -78,12 +101,7 @@ def build_host_asan(objs=None) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed on swa_api.cpp (host ASan)")
     others = [o for o in objs if not o.endswith(os.sep + "swa_api.o")]
-    tmp = HOST_ASAN_LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_ASAN_FLAGS, api_obj,
-           *others, "-o", tmp]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, HOST_ASAN_LIB)
-    return HOST_ASAN_LIB
+    return _link([api_obj, *others], HOST_ASAN_LIB, HOST_ASAN_FLAGS)
 
 
 if __name__ == "__main__":

@@ -234,11 +234,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
                 }
             }
         }
+        SWA_DEBUG_BARRIER();   // every wave's reads of this stage are done
         if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
     }
 
     if (qpos < 0) return;
+    SWA_DCHECK(qpos < p.N && hq < p.Hq);
     // dq^T block: element (db, jq*4 + e) is dim acc_dim(db, jq, half) + e of query l32
     __bf16* op = (__bf16*)bp.dq + (((size_t)b * p.N + qpos) * p.Hq + hq) * D;
 #pragma unroll
@@ -410,6 +412,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
 #pragma unroll
         for (int u = 0; u < Q::PER_THREAD; u++) {
             const int qrow = min(q0 + row0 + u * Q::ROW_STEP, q_hi);
+            SWA_DCHECK(qrow >= 0 && r + qrow * p.dil < p.N && hq < p.Hq);
             const size_t off =
                 (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
             qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
@@ -423,6 +426,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
 #pragma unroll
         for (int u = 0; u < Q::PER_THREAD; u++) {
             const int rw = row0 + u * Q::ROW_STEP;
+            SWA_DCHECK(rw < BQ && stage < NS);
             *(u32x4*)(qs + rw * Q::QP + cc * 8) = qr[u];
             *(u32x4*)(gs + rw * Q::QP + cc * 8) = gr[u];
         }
@@ -558,6 +562,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
         __builtin_amdgcn_sched_barrier(0);
         // stage (st + 2) % NS held tile st - 1, which every wave finished before
         // the previous barrier
+        SWA_DEBUG_BARRIER();
         store_step(stage_store);
         __syncthreads();
     };
@@ -567,6 +572,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
     }
 
     if (!key_ok) return;
+    SWA_DCHECK(kpos >= 0 && kpos < p.N);
     const size_t ko = (((size_t)b * p.N + kpos) * p.Hkv + kvh) * D;
     __bf16* dkp = (__bf16*)bp.dk + ko;
     __bf16* dvp = (__bf16*)bp.dv + ko;
@@ -623,5 +629,9 @@ hipError_t launch_bwd_delta(const BwdParams& p, int D, int dtype, hipStream_t s)
     if (dtype == SWA_BF16) return D == 128 ? launch_delta<128, __bf16>(p, s) : launch_delta<64, __bf16>(p, s);
     return D == 128 ? launch_delta<128, float>(p, s) : launch_delta<64, float>(p, s);
 }
+
+#ifdef SWA_DEBUG
+SWA_DEBUG_COUNTER_READER(debug_counter_bwd_bf16)
+#endif
 
 }  // namespace swa

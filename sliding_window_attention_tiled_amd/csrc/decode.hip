@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(unsigned char* kc, unsig
                                                         int32_t* head, int32_t* len, int Hkv,
                                                         int W, int row_bytes) {
     const int b = blockIdx.x;
+    SWA_DCHECK(head[b] >= 0 && head[b] < W && len[b] >= 0 && len[b] <= W);
     const int slot = min(max(head[b], 0), W - 1);  // device data: keep the write in the ring
     const int chunks = Hkv * row_bytes / 16;  // 16-byte chunks per tensor
     for (int ci = threadIdx.x; ci < chunks; ci += blockDim.x) {
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(256) void kv_append_chunk_kernel(
     const int c = (int)(ci % cpr);
     const int h = (int)((ci / cpr) % Hkv);
     const int64_t t = n - m + ci / ((int64_t)cpr * Hkv);
+    SWA_DCHECK(head[b] >= 0 && head[b] < W);
     const int64_t h0 = min(max(head[b], 0), W - 1);
     const int64_t slot = (h0 + t) % W;
     const size_t src = (((size_t)b * n + t) * Hkv + h) * row_bytes + c * 16;
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(64) void ring_advance_kernel(int32_t* head, int32_t
                                                          int W, int n) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= B) return;
+    SWA_DCHECK(head[b] >= 0 && head[b] < W);
     const int64_t h0 = min(max(head[b], 0), W - 1);
     head[b] = (int32_t)((h0 + n) % W);
     len[b] = (int32_t)min<int64_t>((int64_t)max(len[b], 0) + n, W);
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(256) void kv_append_paged_kernel(
     const int64_t t = n - m + ci / ((int64_t)cpr * Hkv);
     const int64_t pos = (int64_t)max(seq_len[b], 0) + t;
     int page = table[(size_t)b * nb + (int)((pos >> page_shift) % nb)];
+    SWA_DCHECK(seq_len[b] >= 0 && page >= 0 && page < n_pages);
     page = min(max(page, 0), n_pages - 1);
     const int64_t slot = pos & ((1 << page_shift) - 1);
     const size_t src = (((size_t)b * n + t) * Hkv + h) * row_bytes + c * 16;
@@ -117,6 +121,7 @@ __device__ __forceinline__ size_t paged_row(const DecodeParams& p, int b, int kv
                                             int i, int D) {
     const int pos = pos0 + i;
     int page = p.block_table[(size_t)b * p.nb + ((pos >> p.page_shift) % p.nb)];
+    SWA_DCHECK(page >= 0 && page < p.n_pages);
     page = min(max(page, 0), p.n_pages - 1);
     return ((((size_t)page * p.Hkv + kvh) << p.page_shift) + (pos & ((1 << p.page_shift) - 1))) *
            D;
@@ -170,6 +175,7 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
     const int pos0 = seq_n - n_live;
     const int cache_len = PAGED ? n_live : p.cache_len[b];
     const bool full = cache_len >= W;
+    SWA_DCHECK(PAGED || (ring_head >= 0 && ring_head < W && cache_len >= 0 && cache_len <= W));
 
     // ring slots of this wave
     const int s_lo = s * p.slots_per_split;
@@ -221,6 +227,7 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
         lane_pages = nblk <= 64;
         if (lane_pages && lane < nblk) {
             const int pg = p.block_table[(size_t)b * p.nb + ((fb + lane) % p.nb)];
+            SWA_DCHECK(pg >= 0 && pg < p.n_pages);
             my_page = min(max(pg, 0), p.n_pages - 1);
         }
     }
@@ -253,6 +260,7 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             const int key = ci / C::CPR, cc = ci % C::CPR;
             const int pg = PAGED && lane_pages ? lane_page(base + key) : 0;
             if (base + key < hi && (!PAGED || base + key < n_live)) {
+                SWA_DCHECK(base + key >= 0 && base + key < (sk ? n_sk : W));
                 const size_t off = (PAGED ? page_row(base + key, pg)
                                           : (size_t)(base + key) * D) + cc * 8;
                 kr[u] = __builtin_nontemporal_load((const u32x4*)(kb + off));
@@ -665,5 +673,9 @@ hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t 
     }
     return hipGetLastError();
 }
+
+#ifdef SWA_DEBUG
+SWA_DEBUG_COUNTER_READER(debug_counter_decode)
+#endif
 
 }  // namespace swa

@@ -5,6 +5,47 @@
 
 namespace swa {
 
+// ---- debug build (-DSWA_DEBUG) ---------------------------------------------------
+// SWA_DCHECK(cond) states an index contract of a kernel: a global row inside
+// its tensor, a ring slot inside the ring, an LDS offset inside the tile, a
+// device-side index (ring head, page id) inside its range before the kernel
+// clamps it.  The debug build counts each failed check (one vector atomic add
+// to a counter per translation unit) and carries on with the access, which the
+// release code keeps in bounds anyway, so a broken contract is reported
+// without faulting the device.  SWA_DEBUG_BARRIER() is an extra workgroup
+// barrier at points where the release code relies on its own, weaker
+// ordering: with it, phases that the release kernels overlap run one after
+// the other, so a result that differs from the release build's in any bit
+// points at a missing wait or barrier.  Both compile to nothing in release.
+#ifdef SWA_DEBUG
+static __device__ unsigned swa_debug_count;
+#define SWA_DCHECK(cond)                                      \
+    do {                                                      \
+        if (!(cond)) atomicAdd(&::swa::swa_debug_count, 1u);  \
+    } while (0)
+#define SWA_DEBUG_BARRIER() __syncthreads()
+// Defines a host function `name` that reads (and optionally clears) the
+// counter of the translation unit it is placed in.
+#define SWA_DEBUG_COUNTER_READER(name)                                                 \
+    hipError_t name(unsigned* value, bool reset) {                                      \
+        hipError_t e = hipMemcpyFromSymbol(value, HIP_SYMBOL(::swa::swa_debug_count),   \
+                                           sizeof(unsigned), 0, hipMemcpyDeviceToHost); \
+        if (e == hipSuccess && reset) {                                                 \
+            const unsigned zero = 0;                                                    \
+            e = hipMemcpyToSymbol(HIP_SYMBOL(::swa::swa_debug_count), &zero,            \
+                                  sizeof(unsigned), 0, hipMemcpyHostToDevice);          \
+        }                                                                               \
+        return e;                                                                       \
+    }
+#else
+#define SWA_DCHECK(cond) \
+    do {                 \
+    } while (0)
+#define SWA_DEBUG_BARRIER() \
+    do {                    \
+    } while (0)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -100,6 +100,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             qres[qb] = 0;
             qpos[qb] = row < p.n_global ? p.gpos[row] : -1;
         }
+        SWA_DCHECK(qpos[qb] < p.N && hq < p.Hq && b < p.B);
         const __bf16* qp = (const __bf16*)p.q +
                            (((size_t)b * p.N + max(qpos[qb], 0)) * p.Hq + hq) * D + half * 8;
 #pragma unroll
@@ -259,6 +260,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         // before them makes the compiler wait for it ahead of the first MFMA
         // (their results may reuse the loads' address registers).  The loads
         // then overlap the softmax and P V, and are stored after them.
+        SWA_DEBUG_BARRIER();   // every wave's score reads of this stage are done
         if (has_next)
             load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p,
                                 tile_at(j + 1), gk_lds[st ^ 1], gpos_lds);
@@ -426,6 +428,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             }
         }
         if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
+        SWA_DEBUG_BARRIER();   // every wave's P V reads of this stage are done
         if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
     }
@@ -452,6 +455,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                     (m_run[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
         } else {
             const int gi = wave_row0 + qb * 32 + l32;
+            SWA_DCHECK(gi < p.n_global && chunk < p.g_nchunks);
             float* rec = p.partials +
                          ((((size_t)b * p.Hq + hq) * p.n_global + gi) * p.g_nchunks + chunk) *
                              (D + kPartialPad);
@@ -519,5 +523,9 @@ hipError_t launch_fwd_bf16(const FwdParams& band, int D, hipStream_t s) {
     if (D == 128) return w8 ? launch_d<128, kQB, 8>(p, s) : launch_d<128, kQB, 4>(p, s);
     return w8 ? launch_d<64, kQB, 8>(p, s) : launch_d<64, kQB, 4>(p, s);
 }
+
+#ifdef SWA_DEBUG
+SWA_DEBUG_COUNTER_READER(debug_counter_fwd_bf16)
+#endif
 
 }  // namespace swa

@@ -141,6 +141,8 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
             const int r = row0 + 4 * u + q;
             const int chunk = (tid & 15) ^ (is_v ? chunk_xor<true>(q) : chunk_xor<false>(q));
             const int kk = min(ks.k_lo + t * BN + r, ks.k_hi);
+            SWA_DCHECK(kk >= 0 && ks.r + kk * ks.dil < p.N && chunk < 16);
+            SWA_DCHECK(slot_b + (row0 / 4 + u) * GRP * 2 + 1024 <= lds_b + NSLOT * SLOT * 2);
             const __bf16* src = base + (size_t)(ks.r + kk * ks.dil) * rowstride + chunk * 8;
             load_lds_x4(src, slot_b + (unsigned)((row0 / 4 + u) * GRP * 2));
         }
@@ -169,6 +171,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
         for (int u = 0; u < LOADS; u++) {
             const __bf16* ubase =
                 base + (size_t)(ks.r + (ks.k_lo + t * BN + row0 + 4 * u) * ks.dil) * rowstride;
+            SWA_DCHECK(ks.k_lo + t * BN + row0 + 4 * u + 3 <= ks.k_hi &&
+                       ks.r + (ks.k_lo + t * BN + row0 + 4 * u + (int)q) * ks.dil < p.N);
+            SWA_DCHECK(slot_b + (row0 / 4 + u) * GRP * 2 + 1024 <= lds_b + NSLOT * SLOT * 2);
             load_lds_x4(ubase, off, slot_b + (unsigned)((row0 / 4 + u) * GRP * 2));
         }
     };
@@ -260,6 +265,11 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
 
     for (int t = 0;; t++) {
         // ======== matrix phase ==================================================
+        // (debug build: this barrier and the one opening the vector phase make
+        // the two groups' phases run one after the other, in an order that
+        // keeps every ordering the release schedule relies on; both groups
+        // pass the same number of them)
+        SWA_DEBUG_BARRIER();
         __builtin_amdgcn_s_setprio(1);
         // classify tile t for this wave (wave-uniform; nothing at t = n)
         const int kt0 = ks.k_lo + t * BN;
@@ -320,6 +330,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
         __syncthreads();
 
         // ======== vector phase ==================================================
+        SWA_DEBUG_BARRIER();
         __builtin_amdgcn_s_setprio(0);
         // this group's rows of tile t + 2, into the slot of tile t - 1
         const bool load2 = t + 2 < n;
@@ -328,6 +339,9 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
                 load_tile_rows_fast(my_src, my_lds, my_v, t + 2, my_row0);
             else
                 load_tile_rows(my_src, my_lds, my_v, t + 2, my_row0);
+#ifdef SWA_DEBUG
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads complete at once
+#endif
         }
         if (act) {
             if (need_mask) {
@@ -410,6 +424,7 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
     const float l_lane = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
     const float l_tot = l_lane + lane_xor32(l_lane);
     if (qpos < 0) return;
+    SWA_DCHECK(qpos < p.N && hq < p.Hq);
     const float inv = 1.0f / l_tot;
     __bf16* op = (__bf16*)p.out + (((size_t)b * p.N + qpos) * p.Hq + hq) * D;
 #pragma unroll
@@ -436,5 +451,9 @@ hipError_t launch_fwd_pp(const FwdParams& p, hipStream_t s) {
     hipLaunchKernelGGL(swa_fwd_pp_kernel, dim3(p.n_blocks), dim3(512), 0, s, p);
     return hipGetLastError();
 }
+
+#ifdef SWA_DEBUG
+SWA_DEBUG_COUNTER_READER(debug_counter_fwd_pp)
+#endif
 
 }  // namespace swa

@@ -199,6 +199,27 @@ const char* swa_status_string(int status) {
 
 int swa_version(void) { return 100; }
 
+int swa_debug_violations(unsigned long long* count, int reset) {
+#ifdef SWA_DEBUG
+    if (hipDeviceSynchronize() != hipSuccess) return SWA_ERR_HIP;
+    hipError_t (*const readers[])(unsigned*, bool) = {
+        swa::debug_counter_fwd_bf16, swa::debug_counter_fwd_pp, swa::debug_counter_bwd_bf16,
+        swa::debug_counter_decode};
+    unsigned long long total = 0;
+    for (auto read : readers) {
+        unsigned v = 0;
+        if (read(&v, reset != 0) != hipSuccess) return SWA_ERR_HIP;
+        total += v;
+    }
+    if (count != nullptr) *count = total;
+    return SWA_OK;
+#else
+    (void)count;
+    (void)reset;
+    return SWA_ERR_UNSUPPORTED;
+#endif
+}
+
 size_t swa_fwd_workspace_size(int B, int Hq, int N, int D, int n_global) {
     if (B <= 0 || Hq <= 0 || N <= 0 || N > kMaxN || !supported_d(D) || n_global < 0) return 0;
     if (n_global == 0) return 0;

@@ -188,4 +188,13 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int D, bool paged, hipStrea
 hipError_t launch_decode_f32(const DecodeParams& p, int D, bool paged, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t s);
 
+#ifdef SWA_DEBUG
+// Debug build: read (and optionally clear) the failed-check counter of one
+// kernel source file on the current device.
+hipError_t debug_counter_fwd_bf16(unsigned* value, bool reset);
+hipError_t debug_counter_fwd_pp(unsigned* value, bool reset);
+hipError_t debug_counter_bwd_bf16(unsigned* value, bool reset);
+hipError_t debug_counter_decode(unsigned* value, bool reset);
+#endif
+
 }  // namespace swa

@@ -56,10 +56,12 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
             const __bf16* ks_src = nullptr;
             const __bf16* vs_src = nullptr;
             if (kk < 0) {
+                SWA_DCHECK(kk >= -p.W && (unsigned)ring_slot(ks, kk, p.W) < (unsigned)p.W);
                 const size_t off = (size_t)ring_slot(ks, kk, p.W) * T::CPR * 8 + c * 8;
                 ks_src = krbase + off;
                 vs_src = vrbase + off;
             } else if (kk <= ks.k_hi) {
+                SWA_DCHECK(kk < p.N);
                 const size_t off = (size_t)kk * rowstride + c * 8;
                 ks_src = kbase + off;
                 vs_src = vbase + off;
@@ -76,6 +78,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
 #pragma unroll
         for (int u = 0; u < T::PER_THREAD; u++) {
             const int kk = min(kk0 + u * T::KEY_STEP, ks.k_hi);
+            SWA_DCHECK(kk >= 0 && ks.r + kk * ks.dil < p.N);
             const size_t off = (size_t)(ks.r + kk * ks.dil) * rowstride + c * 8;
             kr[u] = *(const u32x4*)(kbase + off);
             vr[u] = *(const u32x4*)(vbase + off);
@@ -100,6 +103,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
 #pragma unroll
     for (int u = 0; u < T::PER_THREAD; u++) {
         if (kpos[u] >= 0) {
+            SWA_DCHECK(kpos[u] < p.N);
             const size_t off = (size_t)kpos[u] * rowstride + c * 8;
             kr[u] = *(const u32x4*)(kbase + off);
             vr[u] = *(const u32x4*)(vbase + off);
@@ -119,6 +123,7 @@ __device__ __forceinline__ void store_tile(const u32x4 (&kr)[T::PER_THREAD],
 #pragma unroll
     for (int u = 0; u < T::PER_THREAD; u++) {
         const int key = key0 + u * T::KEY_STEP;
+        SWA_DCHECK(key < BN);
         *(u32x4*)(stage + key * T::KP + c * 8) = kr[u];
         *(u32x4*)(stage + T::K_ELEMS + key * T::VP + c * 8) = vr[u];
     }
