@@ -35,6 +35,8 @@
 // (acc, m, l) that the combine kernel merges.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "fwd_common.h"
 #include "swa_kernels.h"
@@ -49,8 +51,15 @@ constexpr int kQB = 1;  // 32-query blocks per wave
 // GROWS = false: band workgroups, with gathered tiles of the global keys
 //                after the band when GLOB.
 // GROWS = true : global query rows over one key chunk, partial output.
+// Waves per SIMD the register allocation must leave room for.  Four-wave
+// workgroups with one 32-row block per wave: two at D = 128 (two workgroups
+// per CU), three at D = 64, where three workgroups' tiles fit in LDS and the
+// kernel fits in 168 registers without spilling.
+template <int D, int QB, int NW>
+constexpr int kFwdWavesPerSimd = (QB == 1 && NW == 4) ? (D == 64 ? 3 : 2) : 1;
+
 template <int D, int QB, int NW, bool GROWS, bool GLOB>
-__global__ __launch_bounds__(64 * NW, (QB == 1 && NW == 4) ? 2 : 1)
+__global__ __launch_bounds__(64 * NW, (kFwdWavesPerSimd<D, QB, NW>))
 void swa_fwd_bf16_kernel(const FwdParams p) {
     constexpr bool kGathered = GLOB && !GROWS;
     using T = TileCfg<D, NW>;
@@ -163,39 +172,33 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     }
     __syncthreads();
 
-    // Without dilation the global keys a band row must not see again form
-    // index ranges of the sorted global list (published in gpos_lds by the
-    // barrier above): those inside the row's window, [g_in0, g_in1), and
-    // (causal) those after the row, from g_end on.  Entry gi of a gathered
-    // tile is visible to the row exactly when gi < g_in0 or g_in1 <= gi <
-    // g_end, so the tile's masks need two compares per element.
-    int g_in0[QB], g_in1[QB], g_end[QB];
-    const bool g_ranges = kGathered && ks.dil == 1;
-    if (g_ranges) {
-        // first entry >= x; the same number of steps on every lane
-        auto lower = [&](int x) {
-            int pos = 0;
-            for (int step = 1 << (31 - __builtin_clz(p.n_global)); step > 0; step >>= 1)
-                if (pos + step <= p.n_global && gpos_lds[pos + step - 1] < x) pos += step;
-            return pos;
-        };
-#pragma unroll
-        for (int qb = 0; qb < QB; qb++) {
-            const int i = qres[qb];   // the position (d = 1, r = 0)
-            g_in0[qb] = lower(i - p.wl);
-            g_in1[qb] = lower(i + p.wr + 1);
-            g_end[qb] = p.causal ? lower(i + 1) : p.n_global;
-        }
-    }
 
-    for (int j = 0; j < ks.n_tiles; j++) {
+    // One step of the key stream: tile j in stage j & 1.  GATH: tile j is a
+    // gathered global-key tile (compile time), so that the band tiles run a
+    // loop with only the band masks and band loads, and the gathered tiles
+    // (after the band) a copy with only theirs: one loop body for both kept
+    // every path's values live across the band and took more registers than
+    // the band needs.  The band loop does not prefetch the first gathered
+    // tile; its step loads it.  (Launches with global tokens have no ring
+    // prefix, so the band loads there are plain row loads.)
+    const int n_main = kGathered ? min(ks.n_band_tiles, ks.n_tiles) : ks.n_tiles;
+    auto step = [&](const int j, auto gath_tag) {
+        constexpr bool GATH = decltype(gath_tag)::value;
+        constexpr bool kBandLoads = GROWS || (kGathered && !GATH);
         const int st = j & 1;
-        const bool has_next = j + 1 < ks.n_tiles;
-
+        const bool has_next = j + 1 < (GATH ? ks.n_tiles : n_main);
+        if constexpr (GATH) {
+            if (j == n_main) {
+                load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p,
+                                    tile_at(j), gk_lds[st], gpos_lds);
+                store_tile<T>(kr, vr, smem + st * T::STAGE);
+                __syncthreads();
+            }
+        }
 
         // classify this tile for this wave (wave-uniform)
         const int jt = tile_at(j);
-        const bool band_tile = GROWS || !kGathered || jt < ks.n_band_tiles;
+        constexpr bool band_tile = !GATH;
         const int kt0 = ks.k_lo + jt * BN;
         bool skip = false, need_mask = true;
         // a gathered tile with at most 32 entries: its second 32-key block is
@@ -262,8 +265,8 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         // then overlap the softmax and P V, and are stored after them.
         SWA_DEBUG_BARRIER();   // every wave's score reads of this stage are done
         if (has_next)
-            load_tile<T, GROWS>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p,
-                                tile_at(j + 1), gk_lds[st ^ 1], gpos_lds);
+            load_tile<T, kBandLoads>(kr, vr, kbase, vbase, krbase, vrbase, rowstride, ks, p,
+                                     tile_at(j + 1), gk_lds[st ^ 1], gpos_lds);
         if (!skip) {
             // Element masks.  Lane key offsets within the tile are
             // kb*32 + (e>>2)*8 + half*4 + (e&3); all compares are per element.
@@ -302,23 +305,6 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                                 const int ko = kb * 32 + (e >> 2) * 8 + (e & 3);
                                 if ((unsigned)(ko - lo) > span) s[qb][kb][e] = -INFINITY;
                             }
-                    }
-                } else if (g_ranges) {
-                    // gathered global keys, d = 1: the index ranges above
-#pragma unroll
-                    for (int qb = 0; qb < QB; qb++) {
-                        const unsigned tail = (unsigned)(g_end[qb] - g_in1[qb]);
-#pragma unroll
-                        for (int kb = 0; kb < 2; kb++) {
-                            if (kb == 1 && half_tile) break;
-#pragma unroll
-                            for (int e = 0; e < 16; e++) {
-                                const int gi = gi0 + kb * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-                                const bool vis = gi < g_in0[qb] ||
-                                                 (unsigned)(gi - g_in1[qb]) < tail;
-                                if (!vis) s[qb][kb][e] = -INFINITY;
-                            }
-                        }
                     }
                 } else {
                     // gathered global keys: visible unless already in the band,
@@ -431,7 +417,10 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
         SWA_DEBUG_BARRIER();   // every wave's P V reads of this stage are done
         if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
-    }
+    };
+    for (int j = 0; j < n_main; j++) step(j, std::false_type{});
+    if constexpr (kGathered)
+        for (int j = n_main; j < ks.n_tiles; j++) step(j, std::true_type{});
 
     // ---- epilogue ---------------------------------------------------------------
 #pragma unroll

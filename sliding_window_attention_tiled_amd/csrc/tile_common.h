@@ -19,10 +19,12 @@ struct TileCfg {
     static constexpr int NT = 64 * NW;                          // threads per workgroup
     // LDS row pitches (bf16 elements).  K rows are read 16 B per lane, 16
     // rows per LDS cycle: a pitch of 4 (mod 64) dwords puts those rows on
-    // distinct banks.  V rows are read by ds_read_b64_tr_b16, 4 rows x 64 B per
-    // 32 lanes: a pitch of 16 (mod 64) dwords keeps those on distinct banks.
+    // distinct banks.  V rows are read by ds_read_b64_tr_b16, 4 consecutive
+    // rows x 64 B per 32 lanes: a pitch of 16 or 48 (mod 64) dwords puts the
+    // four rows on four distinct 16-bank quarters.  D + 32 elements is 48
+    // dwords at D = 64 and 80 = 16 (mod 64) at D = 128.
     static constexpr int KP = D + 8;
-    static constexpr int VP = ((D + 95) / 128) * 128 + 32;       // = 32 (mod 128)
+    static constexpr int VP = D + 32;
     static constexpr int K_ELEMS = BN * KP;
     static constexpr int V_ELEMS = BN * VP;
     static constexpr int STAGE = K_ELEMS + V_ELEMS;
