@@ -38,8 +38,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
-FWD_SOURCES = ["sliding_window_attention_tiled_amd/csrc/fwd_bf16.hip",
-               "sliding_window_attention_tiled_amd/csrc/fwd_pp.hip",
+# the sources the headline kernel (swa_fwd_pp_kernel) is compiled from
+FWD_SOURCES = ["sliding_window_attention_tiled_amd/csrc/fwd_pp.hip",
                "sliding_window_attention_tiled_amd/csrc/tile_common.h",
                "sliding_window_attention_tiled_amd/csrc/fwd_common.h",
                "sliding_window_attention_tiled_amd/csrc/device_common.h",
