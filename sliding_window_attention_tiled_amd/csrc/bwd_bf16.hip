@@ -310,8 +310,16 @@ __device__ __forceinline__ TrFrag<D> read_tr_frag(const unsigned short* Qs, int 
     return f;
 }
 
+// At D = 128 a wave's accumulators (dk, dv: 128 registers), K and V (64) and
+// two steps' scores (128) need one wave per SIMD, and the wave overlaps its
+// own work (the next step's scores beside this step's exponentials).  At D =
+// 64 one step's scores fit beside the rest in 256 registers: two waves share
+// each SIMD and overlap each other, and a step runs in plain order.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams bp) {
+constexpr bool kDkdvPipelined = D == 128;
+
+template <int D>
+__global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf16_kernel(const BwdParams bp) {
     using Q = QTileCfg<D>;
     const FwdParams& p = bp.f;
     constexpr int KC = D / 16;
@@ -449,10 +457,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
         load_step(1);
         store_step(1);
         __syncthreads();
-        sc[0][0] = sc[0][1] = dpc[0][0] = dpc[0][1] = f32x16{};
+        if constexpr (kDkdvPipelined<D>) {
+            sc[0][0] = sc[0][1] = dpc[0][0] = dpc[0][1] = f32x16{};
 #pragma unroll
-        for (int kc = 0; kc < KC; kc++)
-            scores(sc[0], dpc[0], kc, read_score_frag<D>(qsm[0], kc, l32, half));
+            for (int kc = 0; kc < KC; kc++)
+                scores(sc[0], dpc[0], kc, read_score_frag<D>(qsm[0], kc, l32, half));
+        }
     }
 
     // One step: tile st in stage st % NS, its scores in set PAR.  The source
@@ -566,9 +576,89 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(const BwdParams b
         store_step(stage_store);
         __syncthreads();
     };
-    for (int st = 0; st < n_steps; st += 2) {
-        step(st, std::integral_constant<int, 0>{});
-        if (st + 1 < n_steps) step(st + 1, std::integral_constant<int, 1>{});
+    // One step in plain order (two waves per SIMD): tile st + 2's rows into
+    // registers, this step's S and dP, their masks, P and dS, the dk/dv
+    // MFMAs, then the store of tile st + 2 into the stage tile st - 1 held.
+    auto step_plain = [&](int st) {
+        const int stage = st % NS;
+        const int stage_store = (st + 2) % NS;
+        const int q0 = q_lo + (st % n_qt) * BQ;
+        const int q1 = q0 + BQ - 1;
+        const bool need_mask = !(q0 >= wk1 - p.wr && q1 <= wk0 + p.wl && q1 <= q_hi &&
+                                 wk0 + 31 <= kb1);
+        load_step(st + 2);
+        const unsigned short* Qs = qsm[stage];
+        const float* lse2 = rsm[stage];
+        const float* dlt = lse2 + BQ;
+        f32x16 s[2], dp[2];
+        s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+        ScoreFrag<D> fr[2];
+        fr[0] = read_score_frag<D>(Qs, 0, l32, half);
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            if (kc + 1 < KC) fr[(kc + 1) & 1] = read_score_frag<D>(Qs, kc + 1, l32, half);
+            scores(s, dp, kc, fr[kc & 1]);
+        }
+        if (need_mask) {
+            // as in the pipelined step: query - key + wr in [0, wl + wr], query
+            // <= q_hi, key <= kb1
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) {
+                const int base = q0 + rb * 32 + half * 4 - key + p.wr;
+                const int qlim = q_hi - (q0 + rb * 32 + half * 4);
+                const int kbad = kb1 - key;
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const int ro = (e >> 2) * 8 + (e & 3);
+                    const int bad = ((base + ro) | (span - base - ro) | (qlim - ro) | kbad) >> 31;
+                    s[rb][e] += __builtin_bit_cast(float, bad & 0xff800000);
+                }
+            }
+        }
+        // P and dS of the step's four 16-query steps (8 elements each per lane)
+        bf16x8 pb[4], dsb[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const int rowb = (t >> 1) * 32 + (t & 1) * 16 + half * 4;
+            f32x4 lr[4];
+            lr[0] = *(const f32x4*)(lse2 + rowb);
+            lr[1] = *(const f32x4*)(lse2 + rowb + 8);
+            lr[2] = *(const f32x4*)(dlt + rowb);
+            lr[3] = *(const f32x4*)(dlt + rowb + 8);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int el = slot_elem(e);
+                const int ei = (t & 1) * 8 + el;
+                const float pe = fast_exp2(__builtin_fmaf(s[t >> 1][ei], c, -lr[el >> 2][el & 3]));
+                pb[t][e] = (__bf16)pe;
+                dsb[t][e] = (__bf16)(pe * (dp[t >> 1][ei] - lr[2 + (el >> 2)][el & 3]));
+            }
+        }
+        // dv^T += dout^T P and dk^T += Q^T dS over the four 16-query steps
+        TrFrag<D> tf[2];
+        tf[0] = read_tr_frag<D>(Qs, tr_off, 0);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            if (t + 1 < 4) tf[(t + 1) & 1] = read_tr_frag<D>(Qs, tr_off, t + 1);
+#pragma unroll
+            for (int db = 0; db < DB; db++) {
+                dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[t & 1].g[db], pb[t],
+                                                                    dvacc[db], 0, 0, 0);
+                dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tf[t & 1].q[db], dsb[t],
+                                                                    dkacc[db], 0, 0, 0);
+            }
+        }
+        SWA_DEBUG_BARRIER();
+        store_step(stage_store);
+        __syncthreads();
+    };
+    if constexpr (kDkdvPipelined<D>) {
+        for (int st = 0; st < n_steps; st += 2) {
+            step(st, std::integral_constant<int, 0>{});
+            if (st + 1 < n_steps) step(st + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        for (int st = 0; st < n_steps; st++) step_plain(st);
     }
 
     if (!key_ok) return;
