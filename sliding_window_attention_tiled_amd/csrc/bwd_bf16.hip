@@ -98,7 +98,11 @@ struct DqTileCfg : TileCfg<D, NW> {
 
 // Two workgroups per CU: the cap of 256 registers per lane costs a few spills,
 // which the second resident workgroup more than hides.
-template <int D, int NW>
+// GLOB: after the band, gathered tiles of the global keys add the pairs of a
+// row that is not itself global with the global keys outside its band (and,
+// causal, not after it).  A global row's pairs outside its band are the
+// global-row pass's.
+template <int D, int NW, bool GLOB>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams bp) {
     using T = DqTileCfg<D, NW>;
     const FwdParams& p = bp.f;
@@ -107,6 +111,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
 
     __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::STAGE];
     __shared__ __attribute__((aligned(16))) int gk_lds[2][2 * BN];
+    // the global positions for the gathered tile loads (an LDS copy: read
+    // per lane from the parameter block inside the loop, they would add a
+    // wait for vector memory before the next LDS read)
+    __shared__ int gpos_lds[GLOB ? SWA_MAX_GLOBAL : 1];
+    const int* gpos_ptr = GLOB ? gpos_lds : nullptr;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -151,26 +160,56 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
     const float c = p.scale_log2;
 
     u32x4 kr[T::PER_THREAD], vr[T::PER_THREAD];
+    if constexpr (GLOB)
+        for (int i = threadIdx.x; i < p.n_global; i += T::NT) gpos_lds[i] = p.gpos[i];
+    // (tile 0 is a band tile: the gathered loads that read gpos_lds come after
+    // the barrier below)
     if (ks.n_tiles > 0) {
         load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, 0, gk_lds[0],
                             nullptr);
         store_tile<T>(kr, vr, smem);
     }
     __syncthreads();
+    // is the lane's row one of the global positions?  (binary search of the
+    // sorted list; the same number of steps on every lane)
+    bool row_glob = false;
+    if constexpr (GLOB) {
+        int pos = 0;
+        for (int w = 1 << (31 - __builtin_clz(p.n_global)); w > 0; w >>= 1)
+            if (pos + w <= p.n_global && gpos_lds[pos + w - 1] < qpos) pos += w;
+        row_glob = qpos >= 0 && pos < p.n_global && gpos_lds[pos] == qpos;
+    }
 
     const int tr_off = tr_row(lane) * T::KP + tr_col(lane);
-    for (int j = 0; j < ks.n_tiles; j++) {
+    // Band tiles, then (GLOB) the gathered global-key tiles in a copy of the
+    // step of their own, so that the band loop keeps only the band's masks
+    // and row loads.  The band loop does not prefetch the first gathered
+    // tile; its step loads it.
+    const int n_main = GLOB ? min(ks.n_band_tiles, ks.n_tiles) : ks.n_tiles;
+    auto step = [&](const int j, auto gath_tag) {
+        constexpr bool GATH = decltype(gath_tag)::value;
+        constexpr bool kBandLoads = GLOB && !GATH;
         const int st = j & 1;
-        const bool has_next = j + 1 < ks.n_tiles;
+        const bool has_next = j + 1 < (GATH ? ks.n_tiles : n_main);
+        if constexpr (GATH) {
+            if (j == n_main) {
+                load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, j,
+                                    gk_lds[st], gpos_ptr);
+                store_tile<T>(kr, vr, smem + st * T::STAGE);
+                __syncthreads();
+            }
+        }
         const int kt0 = ks.k_lo + j * BN;
         const int kt1 = kt0 + BN - 1;
-        const bool skip = w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl;
-        const bool need_mask = !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
+        const bool skip =
+            !GATH && (w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl);
+        const bool need_mask =
+            GATH || !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
         const unsigned short* Ks = smem + st * T::STAGE;
         const unsigned short* Vs = Ks + T::K_ELEMS;
         if (skip && has_next)
-            load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, j + 1,
-                                gk_lds[st ^ 1], nullptr);
+            load_tile<T, kBandLoads>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p, j + 1,
+                                     gk_lds[st ^ 1], gpos_ptr);
         if (!skip) {
             // one 32-key block at a time: S^T = K Q^T and dP^T = V dout^T for
             // its keys, then dS^T and dq^T += K^T dS^T over its two 16-key
@@ -192,9 +231,32 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
                 // ahead of the MFMAs, whose results may reuse their address
                 // registers)
                 if (kb == 0 && has_next)
-                    load_tile<T, false>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks, p,
-                                        j + 1, gk_lds[st ^ 1], nullptr);
-                if (need_mask) {
+                    load_tile<T, kBandLoads>(kr, vr, kbase, vbase, kbase, vbase, rowstride, ks,
+                                             p, j + 1, gk_lds[st ^ 1], gpos_ptr);
+                if (GATH) {
+                    // gathered global keys (position g, residue coordinate r of
+                    // g): hidden when padding (g < 0), in the row's band, after
+                    // a causal row, or for every key when the row is global
+                    const int* gk = gk_lds[st];
+                    const int span = p.wl + p.wr;
+                    const int causal_mask = p.causal ? -1 : 0;
+                    const int row_bad = row_glob ? -1 : 0;
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; e4++) {
+                        const int4 g4 = *(const int4*)(gk + kb * 32 + e4 * 8 + half * 4);
+                        const int4 r4 = *(const int4*)(gk + BN + kb * 32 + e4 * 8 + half * 4);
+                        const int gv[4] = {g4.x, g4.y, g4.z, g4.w};
+                        const int rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                        for (int e3 = 0; e3 < 4; e3++) {
+                            const int x = rv[e3] - qres + p.wl;
+                            const int inband = ~(x | (span - x)) >> 31;
+                            const int future = causal_mask & ((qpos - gv[e3]) >> 31);
+                            const int bad = (gv[e3] >> 31) | inband | future | row_bad;
+                            s[e4 * 4 + e3] += __builtin_bit_cast(float, bad & 0xff800000);
+                        }
+                    }
+                } else if (need_mask) {
                     // the forward's band edge masks (x = key - query + wl in
                     // [0, wl + wr], key <= k_hi): the lane's valid offsets form
                     // one interval [lo, hi] (an empty one moved past the tile),
@@ -237,7 +299,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
         SWA_DEBUG_BARRIER();   // every wave's reads of this stage are done
         if (has_next) store_tile<T>(kr, vr, smem + (st ^ 1) * T::STAGE);
         __syncthreads();
-    }
+    };
+    for (int j = 0; j < n_main; j++) step(j, std::false_type{});
+    if constexpr (GLOB)
+        for (int j = n_main; j < ks.n_tiles; j++) step(j, std::true_type{});
 
     if (qpos < 0) return;
     SWA_DCHECK(qpos < p.N && hq < p.Hq);
@@ -693,7 +758,12 @@ hipError_t launch_delta(const BwdParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const BwdParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, 4>), dim3(p.f.n_blocks), dim3(256), 0, s, p);
+    if (p.f.n_global > 0)
+        hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, 4, true>), dim3(p.f.n_blocks), dim3(256), 0, s,
+                           p);
+    else
+        hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, 4, false>), dim3(p.f.n_blocks), dim3(256), 0,
+                           s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D>), dim3(p.k_blocks), dim3(256), 0, s, p);

@@ -964,8 +964,10 @@ hipError_t launch_all(const GlobalBwdParams& g, hipStream_t s) {
     if constexpr (std::is_same_v<T, __bf16>) {
         hipLaunchKernelGGL((rows_dq_mfma_kernel<D>), rows_dq_grid, dim3(kMfmaNT), 0, s, g);
         hipLaunchKernelGGL((cols_dkdv_mfma_kernel<D>), cols_dkdv_grid, dim3(kMfmaNT), 0, s, g);
-        hipLaunchKernelGGL((cols_dq_mfma_kernel<D>), cols_dq_grid, dim3(kMfmaNT), 0, s, g);
-        hipLaunchKernelGGL((rows_dkdv_mfma_kernel<D>), rows_dkdv_grid, dim3(kMfmaNT), 0, s, g);
+        if (!(g.fused & kGlobalColsDqFused))
+            hipLaunchKernelGGL((cols_dq_mfma_kernel<D>), cols_dq_grid, dim3(kMfmaNT), 0, s, g);
+        if (!(g.fused & kGlobalRowsDkdvFused))
+            hipLaunchKernelGGL((rows_dkdv_mfma_kernel<D>), rows_dkdv_grid, dim3(kMfmaNT), 0, s, g);
     } else {
         hipLaunchKernelGGL((rows_dq_kernel<D, T>), rows_dq_grid, dim3(NT), 0, s, g);
         hipLaunchKernelGGL((cols_dkdv_kernel<D, T>), cols_dkdv_grid, dim3(NT), 0, s, g);

@@ -584,6 +584,13 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
         bwd_global_chunks(B, Hq, N, &gb.key_chunk, &gb.n_key_chunks);
         bwd_global_chunks(B, Hkv, N, &gb.row_chunk, &gb.n_row_chunks);
         gb.n_row_tiles_all = gb.n_key_tiles_all = (int)cdiv(N, 64);
+        if (dtype == SWA_BF16) {
+            // the bf16 dq pass walks the global keys after the band (gathered
+            // tiles), which covers the pairs of the other rows with them
+            p.n_global = ng;
+            for (int i = 0; i < ng; i++) p.gpos[i] = g[i];
+            gb.fused |= swa::kGlobalColsDqFused;
+        }
         if ((int64_t)B * Hq * gb.n_row_tiles_all > INT32_MAX ||
             (int64_t)B * Hq * gb.row_tiles * gb.n_key_chunks > INT32_MAX ||
             (int64_t)B * Hkv * gb.key_tiles * gb.n_row_chunks > INT32_MAX)

@@ -105,8 +105,12 @@ struct GlobalBwdParams {
     int row_chunk, n_row_chunks;   // row split of the global-key dk/dv pass
     int n_row_tiles_all;  // 64-row tiles of all N rows
     int n_key_tiles_all;  // 64-key tiles of all N keys
+    int fused;            // kGlobalColsDqFused | kGlobalRowsDkdvFused: passes the band
+                          // kernels already did (their launches are skipped)
     int32_t gpos[SWA_MAX_GLOBAL];  // sorted, unique
 };
+constexpr int kGlobalColsDqFused = 1;    // dq of other rows from global keys
+constexpr int kGlobalRowsDkdvFused = 2;  // dk, dv of every key from global rows
 
 struct DecodeParams {
     const void* q;
