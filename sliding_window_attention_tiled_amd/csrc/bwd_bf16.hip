@@ -397,6 +397,15 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
     // per stage: Q tile, dout tile, lse2[BQ], delta[BQ]
     __shared__ __attribute__((aligned(16))) unsigned short qsm[NS][2 * Q::ELEMS];
     __shared__ __attribute__((aligned(16))) float rsm[NS][2 * BQ];
+    // D = 64 with global tokens: after the band's steps, gathered steps stage
+    // the global rows (64 to a tile, for every query head of the group) and
+    // add their pairs with this block's keys outside their band (causal: not
+    // after the row), the global-row dk/dv pairs.  Per stage the rows'
+    // positions (-1: padding) and residue coordinates (this block's class,
+    // else a value no window reaches) feed the masks.
+    constexpr bool kGathRows = !kDkdvPipelined<D>;
+    __shared__ int gpos_lds[kGathRows ? SWA_MAX_GLOBAL : 1];
+    __shared__ __attribute__((aligned(16))) int rpos[kGathRows ? NS : 1][2 * BQ];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -436,7 +445,9 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
     const int q_lo = max(0, kb0 - p.wr);
     const int q_hi = min(Nr - 1, kb1 + p.wl);
     const int n_qt = (q_hi - q_lo + BQ) / BQ;
-    const int n_steps = n_qt * p.group;            // (query head, query tile) pairs
+    const int n_band_steps = n_qt * p.group;       // (query head, query tile) pairs
+    const int n_gt = kGathRows && p.n_global > 0 ? (p.n_global + BQ - 1) / BQ : 0;
+    const int n_steps = n_band_steps + n_gt * p.group;   // then (head, gathered tile)
 
     // the lane's key as the B operand of S = Q K^T and dP = dout V^T
     const int key = wk0 + l32;
@@ -466,28 +477,68 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
     // always takes them) zero P and dS there, and the values are finite.
     u32x4 qr[Q::PER_THREAD], gr[Q::PER_THREAD];
     float rl = 0.f;
+    int rp_pos = -1, rp_res = kFarAway;   // gathered steps: the row of thread t < BQ
+    if (n_gt > 0) {
+        for (int i = threadIdx.x; i < p.n_global; i += 256) gpos_lds[i] = p.gpos[i];
+        __syncthreads();
+    }
     auto load_step = [&](int st) {
         st = min(st, n_steps - 1);
-        const int hq = kvh * p.group + st / n_qt;
-        const int q0 = q_lo + (st % n_qt) * BQ;
+        const bool gth = kGathRows && st >= n_band_steps;   // uniform
+        int hq, q0;
+        if (!gth) {
+            hq = kvh * p.group + st / n_qt;
+            q0 = q_lo + (st % n_qt) * BQ;
+        } else {
+            // q0: index of the tile's first row in the global list
+            hq = kvh * p.group + (st - n_band_steps) / n_gt;
+            q0 = ((st - n_band_steps) % n_gt) * BQ;
+        }
+        // absolute position of tile row rr (band rows past q_hi repeat q_hi;
+        // gathered rows past the list repeat its last entry)
+        auto row_pos = [&](int rr) {
+            return gth ? gpos_lds[min(q0 + rr, p.n_global - 1)]
+                       : r + min(q0 + rr, q_hi) * p.dil;
+        };
+        if constexpr (kGathRows) {
+            const int rr = threadIdx.x & (BQ - 1);
+            rp_pos = gth && q0 + rr < p.n_global ? gpos_lds[q0 + rr] : -1;
+            rp_res = rp_pos >= 0 && rp_pos % p.dil == r ? rp_pos / p.dil : kFarAway;
+        }
         // lse for threads 0..63, delta for 64..127, one row each (later lanes
         // read a row again and drop it, so the load needs no branch).  It is
         // issued before the tile rows and used only when stored (lse scaled to
         // base 2 there): any wait the compiler places around it, for a register
         // kept in scratch say, then cannot include the tile loads, which would
         // stall the step for their whole latency.
+        const int row0 = threadIdx.x / Q::CPR, cc = threadIdx.x % Q::CPR;
+        if constexpr (!kGathRows) {
+            {
+                const int qrow = min(q0 + (int)(threadIdx.x & (BQ - 1)), q_hi);
+                const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
+                rl = *((threadIdx.x < BQ ? p.lse : bp.delta) + li);
+            }
+#pragma unroll
+            for (int u = 0; u < Q::PER_THREAD; u++) {
+                const int qrow = min(q0 + row0 + u * Q::ROW_STEP, q_hi);
+                SWA_DCHECK(qrow >= 0 && r + qrow * p.dil < p.N && hq < p.Hq);
+                const size_t off =
+                    (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
+                qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
+                gr[u] = *(const u32x4*)((const __bf16*)bp.dout + off);
+            }
+            return;
+        }
         {
-            const int qrow = min(q0 + (int)(threadIdx.x & (BQ - 1)), q_hi);
-            const size_t li = ((size_t)b * p.Hq + hq) * p.N + r + (size_t)qrow * p.dil;
+            const int pos = row_pos((int)(threadIdx.x & (BQ - 1)));
+            const size_t li = ((size_t)b * p.Hq + hq) * p.N + pos;
             rl = *((threadIdx.x < BQ ? p.lse : bp.delta) + li);
         }
-        const int row0 = threadIdx.x / Q::CPR, cc = threadIdx.x % Q::CPR;
 #pragma unroll
         for (int u = 0; u < Q::PER_THREAD; u++) {
-            const int qrow = min(q0 + row0 + u * Q::ROW_STEP, q_hi);
-            SWA_DCHECK(qrow >= 0 && r + qrow * p.dil < p.N && hq < p.Hq);
-            const size_t off =
-                (((size_t)b * p.N + r + (size_t)qrow * p.dil) * p.Hq + hq) * D + cc * 8;
+            const int pos = row_pos(row0 + u * Q::ROW_STEP);
+            SWA_DCHECK(pos >= 0 && pos < p.N && hq < p.Hq);
+            const size_t off = (((size_t)b * p.N + pos) * p.Hq + hq) * D + cc * 8;
             qr[u] = *(const u32x4*)((const __bf16*)p.q + off);
             gr[u] = *(const u32x4*)((const __bf16*)bp.dout + off);
         }
@@ -504,6 +555,11 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
             *(u32x4*)(gs + rw * Q::QP + cc * 8) = gr[u];
         }
         if (threadIdx.x < 2 * BQ) rsm[stage][threadIdx.x] = threadIdx.x < BQ ? rl * kLog2e : rl;
+        if constexpr (kGathRows)
+            if (threadIdx.x < BQ) {
+                rpos[stage][threadIdx.x] = rp_pos;
+                rpos[stage][BQ + threadIdx.x] = rp_res;
+            }
     };
 
     const int tr_off = tr_row(lane) * Q::QP + tr_col(lane);
@@ -664,7 +720,32 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
             if (kc + 1 < KC) fr[(kc + 1) & 1] = read_score_frag<D>(Qs, kc + 1, l32, half);
             scores(s, dp, kc, fr[kc & 1]);
         }
-        if (need_mask) {
+        if (kGathRows && st >= n_band_steps) {
+            // gathered global rows: hidden when padding (position < 0), when
+            // the key lies in the row's band (x = row - key + wr in [0, wl +
+            // wr], residue coordinates of this class), after a causal row, or
+            // past kb1
+            const int* rp = rpos[stage];
+            const int causal_mask = p.causal ? -1 : 0;
+            const int kbad = (kb1 - key) >> 31;
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; e4++) {
+                    const int4 p4 = *(const int4*)(rp + rb * 32 + e4 * 8 + half * 4);
+                    const int4 r4 = *(const int4*)(rp + BQ + rb * 32 + e4 * 8 + half * 4);
+                    const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+                    const int rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+                    for (int e3 = 0; e3 < 4; e3++) {
+                        const int x = rv[e3] - key + p.wr;
+                        const int inband = ~(x | (span - x)) >> 31;
+                        const int future = causal_mask & ((pv[e3] - kpos) >> 31);
+                        const int bad = (pv[e3] >> 31) | inband | future | kbad;
+                        s[rb][e4 * 4 + e3] += __builtin_bit_cast(float, bad & 0xff800000);
+                    }
+                }
+        } else if (need_mask) {
             // as in the pipelined step: query - key + wr in [0, wl + wr], query
             // <= q_hi, key <= kb1
 #pragma unroll

@@ -590,6 +590,9 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             p.n_global = ng;
             for (int i = 0; i < ng; i++) p.gpos[i] = g[i];
             gb.fused |= swa::kGlobalColsDqFused;
+            // at D = 64 the dk/dv pass stages the global rows after the band
+            // (gathered steps), which covers their pairs with every key
+            if (D == 64) gb.fused |= swa::kGlobalRowsDkdvFused;
         }
         if ((int64_t)B * Hq * gb.n_row_tiles_all > INT32_MAX ||
             (int64_t)B * Hq * gb.row_tiles * gb.n_key_chunks > INT32_MAX ||
