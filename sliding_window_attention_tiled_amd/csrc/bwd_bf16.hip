@@ -61,6 +61,7 @@ __device__ __forceinline__ int acc_dim(int db, int jq, int h) {
 }
 
 // ---- 1. delta_i = dout_i . out_i ---------------------------------------------------
+// The float32 path's pass (the bf16 dq pass computes delta for its rows).
 // D/8 lanes per row (8 elements each), 256 threads.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* out, const T* dout, float* delta,
@@ -150,7 +151,25 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_bf16_kernel(const BwdParams
     }
     const size_t lrow = ((size_t)b * p.Hq + hq) * p.N + max(qpos, 0);
     const float lse2 = qpos >= 0 ? p.lse[lrow] * kLog2e : 0.f;
-    const float dlt = qpos >= 0 ? bp.delta[lrow] : 0.f;
+    // delta = dout . out of the lane's row, from its half of the row (the
+    // dout fragments above) and the other half's lane; every query row has
+    // one owner lane pair in this pass, which writes it for the dk/dv pass
+    // and the global-token passes that run after it
+    float dlt;
+    {
+        const __bf16* op = (const __bf16*)bp.out +
+                           (((size_t)b * p.N + max(qpos, 0)) * p.Hq + hq) * D + half * 8;
+        float acc = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            const bf16x8 o = qpos >= 0 ? *(const bf16x8*)(op + kc * 16)
+                                       : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+            for (int e = 0; e < 8; e++) acc = __builtin_fmaf((float)o[e], (float)greg[kc][e], acc);
+        }
+        dlt = acc + lane_xor32(acc);
+        if (qpos >= 0 && half == 0) bp.delta[lrow] = dlt;
+    }
     const int w_first = wave_row0;
     const int w_last = min(wave_row0 + 31, ks.Nr - 1);
 
@@ -866,8 +885,8 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t s) {
     return D == 128 ? launch_d<128>(p, s) : launch_d<64>(p, s);
 }
 
-hipError_t launch_bwd_delta(const BwdParams& p, int D, int dtype, hipStream_t s) {
-    if (dtype == SWA_BF16) return D == 128 ? launch_delta<128, __bf16>(p, s) : launch_delta<64, __bf16>(p, s);
+// float32 only: the bf16 dq pass computes delta for its rows itself.
+hipError_t launch_bwd_delta(const BwdParams& p, int D, hipStream_t s) {
     return D == 128 ? launch_delta<128, float>(p, s) : launch_delta<64, float>(p, s);
 }
 

@@ -600,7 +600,10 @@ int swa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             return SWA_ERR_ARG;
     }
 
-    if (swa::launch_bwd_delta(bp, D, dtype, stream) != hipSuccess) return SWA_ERR_HIP;
+    // (bf16: the dq pass computes each row's delta and writes it before the
+    // passes that read it)
+    if (dtype == SWA_F32 && swa::launch_bwd_delta(bp, D, stream) != hipSuccess)
+        return SWA_ERR_HIP;
     hipError_t e = dtype == SWA_BF16 ? swa::launch_bwd_bf16(bp, D, stream)
                                      : swa::launch_bwd_f32(bp, D, stream);
     if (e == hipSuccess && ng > 0) e = swa::launch_bwd_global(gb, D, dtype, stream);

@@ -174,7 +174,7 @@ FwdShape bwd_bf16_dq_shape(int group);
 int bwd_bf16_dkdv_keys();
 FwdShape bwd_f32_dq_shape(int group);
 int bwd_f32_dkdv_keys();
-hipError_t launch_bwd_delta(const BwdParams& p, int D, int dtype, hipStream_t s);
+hipError_t launch_bwd_delta(const BwdParams& p, int D, hipStream_t s);   // float32
 hipError_t launch_bwd_bf16(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, int D, hipStream_t s);
 hipError_t launch_bwd_global(const GlobalBwdParams& g, int D, int dtype, hipStream_t s);
