@@ -46,3 +46,12 @@ def test_encoder_pairs(wl, wr, G):
     c = dict(N=N, win_left=wl, win_right=wr, global_idx=G)
     m = bruteforce.mask_matrix(N, wl, wr, 1, G if G else None)
     assert bench.encoder_pairs(c) == int(m.sum())
+
+
+def test_headline_traffic_profile_matches_the_kernel_sources():
+    """The HBM traffic the bench reports comes from the committed counter
+    summary of the headline kernel, keyed by a hash of the sources it is
+    compiled from; after a change to them the counters must be taken again
+    (or the key renewed when the kernel's code is shown unchanged)."""
+    import bench
+    assert bench.measured_traffic() is not None
