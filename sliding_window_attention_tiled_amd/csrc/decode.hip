@@ -249,6 +249,14 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
         return !PAGED && ck >= n_chunks ? k_lo + (ck - n_chunks) * CH : w_lo + ck * CH;
     };
     auto chunk_end = [&](int ck) -> int { return !PAGED && ck >= n_chunks ? k_hi : w_hi; };
+    // A ring slot that holds no entry (age >= cache_len) is not read: its
+    // bytes are whatever the caller's buffer held, and a zero weight times a
+    // NaN or infinity there would still reach the output.
+    auto slot_live = [&](int slot) {
+        int age = ring_head - 1 - slot;
+        if (age < 0) age += W;
+        return age < cache_len;
+    };
     auto load_chunk = [&](int ck) {
         const bool sk = !PAGED && ck >= n_chunks;
         const int base = chunk_base(ck), hi = chunk_end(ck);
@@ -259,7 +267,8 @@ __global__ __launch_bounds__(DNT, 2) void decode_bf16_kernel(const DecodeParams 
             const int ci = lane + u * 64;
             const int key = ci / C::CPR, cc = ci % C::CPR;
             const int pg = PAGED && lane_pages ? lane_page(base + key) : 0;
-            if (base + key < hi && (!PAGED || base + key < n_live)) {
+            const bool live = PAGED ? base + key < n_live : (sk || full || slot_live(base + key));
+            if (base + key < hi && live) {
                 SWA_DCHECK(base + key >= 0 && base + key < (sk ? n_sk : W));
                 const size_t off = (PAGED ? page_row(base + key, pg)
                                           : (size_t)(base + key) * D) + cc * 8;

@@ -76,3 +76,38 @@ def test_decode_full_rolling_cache():
     gen = DecodeInputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["W"], c["D"], c["dtype"])
     steps = c["steps"]
     _run_steps(gen, steps, {0, 1, 100, 200, steps - 1}, c["dtype"], "rolling cache")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_never_reads_stale_slots(dt):
+    """Slots that hold no entry (age >= cache_len) may contain anything,
+    NaN and infinities included: the result must equal the oracle's, which
+    attends only the live entries.  Live ranges wrap around slot 0, and one
+    sequence holds a single entry."""
+    B, Hq, Hkv, W, D = 3, 8, 2, 300, 128
+    rng = np.random.Generator(np.random.PCG64(81))
+    ring_head = np.array([5, 290, 0], np.int32)
+    cache_len = np.array([37, 299, 1], np.int32)
+    shape = (B, Hkv, W, D)
+    kc = rng.standard_normal(shape, dtype=np.float32)
+    vc = rng.standard_normal(shape, dtype=np.float32)
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32)
+    poison = np.array([np.nan, np.inf, -np.inf], np.float32)
+    for b in range(B):
+        for s in range(W):
+            age = (ring_head[b] - 1 - s) % W
+            if age >= cache_len[b]:
+                kc[b, :, s] = poison[s % 3]
+                vc[b, :, s] = poison[(s + 1) % 3]
+    if dt == "bf16":
+        from sliding_window_attention_tiled_amd.inputs import to_bf16_bits
+        kc, vc, q = to_bf16_bits(kc), to_bf16_bits(vc), to_bf16_bits(q)
+    log(f"[decode] stale slots poisoned, {dt}")
+    ring = oracle.ring(kc, vc, ring_head, cache_len)
+    ref_o, ref_l = ring.decode(q)
+    out, lse = binding.decode(to_dev(q), to_dev(kc), to_dev(vc),
+                              torch.from_numpy(ring_head).to("cuda"),
+                              torch.from_numpy(cache_len).to("cuda"))
+    torch.cuda.synchronize()
+    check(to_host_f64(out), ref_o, dt, f"stale-slot decode {dt} out")
+    check(to_host_f64(lse), ref_l, dt, f"stale-slot decode {dt} lse")
