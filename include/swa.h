@@ -382,11 +382,17 @@ int swa_decode_paged(const void* q, const void* kpool, const void* vpool,
  *                        of the global keys it attends (aiqz.cc "Sliding
  *                        window attention: Mistral", section "global attention
  *                        tokens").  The pairs outside the band are summed in
- *                        float32 and added to the band's dq, dk, dv (one more
- *                        rounding of those rows in bf16).  Work split over
- *                        key or row chunks writes one float32 partial per
- *                        chunk, summed in chunk order: no atomics, and the
- *                        same call gives the same bits every time.
+ *                        float32.  In bf16 the pairs of ordinary rows with
+ *                        global keys join their row's dq before its one
+ *                        rounding, and at D = 64 so do the global rows'
+ *                        pairs with every key in that key's dk, dv; the
+ *                        other such terms (a global row's dq, a global key's
+ *                        dk and dv, and float32 or D = 128 where no band pass
+ *                        takes them) are added to the band's result, one more
+ *                        rounding of those rows in bf16.  Work split over key
+ *                        or row chunks writes one float32 partial per chunk,
+ *                        summed in chunk order: no atomics, and the same call
+ *                        gives the same bits every time.
  *   workspace            device scratch of swa_bwd_workspace_size() bytes
  *                        (per-row dout . out; with global tokens also the
  *                        float32 partials of their rows and keys); two calls

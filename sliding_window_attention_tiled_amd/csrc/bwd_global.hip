@@ -17,8 +17,11 @@
 //   cols_dq    dq of non-global rows over E_col, read-modify-write
 //   cols_dkdv  dk, dv of global keys over E_col, one float32 partial per row chunk
 //   add_dq / add_dkdv sum the partials in chunk order into dq / dk, dv.
-// Every sum has a fixed order (no atomics), so the backward is bitwise
-// repeatable.
+// In bf16 the band dq pass walks the global keys after its band (cols_dq is
+// not launched), and at D = 64 the band dk/dv pass stages the global rows
+// after its band (rows_dkdv is not launched): GlobalBwdParams::fused says
+// which.  Every sum has a fixed order (no atomics), so the backward is
+// bitwise repeatable.
 // bf16 runs them on MFMA with the global tokens of a 16-wide block as the
 // columns of 16x16 tiles; float32 runs them on the vector ALUs, rows (or keys)
 // of a workgroup spread over lanes with tiles of 32 partners staged in LDS.
