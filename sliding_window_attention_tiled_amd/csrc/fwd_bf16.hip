@@ -121,18 +121,11 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     const int w_last = min(wave_row0 + 32 * QB - 1, ks.Nr - 1);
 
     f32x16 oacc[QB][DB];
-    float m_run[QB], l_run[QB];
-    // D = 64: the row sums come from an MFMA with an all-ones A operand (every
-    // row of ones x P^T is the sum over the step's keys of the lane's query
-    // column, both halves included); the matrix cores have room there, the
-    // vector ALUs do not.  D = 128 sums in the lane with dot2.
-    constexpr bool kSumMfma = D == 64;
-    f32x16 lacc[QB];
+    float m_run[QB], l_run[QB];   // l_run: the lane's half of the row sum (dot2)
 #pragma unroll
     for (int qb = 0; qb < QB; qb++) {
         m_run[qb] = kEmptyMax;
         l_run[qb] = 0.f;
-        lacc[qb] = f32x16{};
 #pragma unroll
         for (int db = 0; db < DB; db++) oacc[qb][db] = f32x16{};
     }
@@ -353,7 +346,6 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                 if (__any(up)) {
                     const float alpha = fast_exp2(m_run[qb] - m_use[qb]);
                     l_run[qb] *= alpha;
-                    if (kSumMfma) lacc[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; db++) oacc[qb][db] *= alpha;
                 }
@@ -388,15 +380,13 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                     for (int e = 0; e < 8; e++)
                         pb[qb][e] = (__bf16)fast_exp2(
                             __builtin_fmaf(s[qb][t >> 1][(t & 1) * 8 + e], c, -m_use[qb]));
-                    if (!kSumMfma) {
-                        float ls = l_run[qb];
+                    float ls = l_run[qb];
 #pragma unroll
-                        for (int e = 0; e < 4; e++) {
-                            const bf16x2 pr = {pb[qb][2 * e], pb[qb][2 * e + 1]};
-                            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
-                        }
-                        l_run[qb] = ls;
+                    for (int e = 0; e < 4; e++) {
+                        const bf16x2 pr = {pb[qb][2 * e], pb[qb][2 * e + 1]};
+                        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
                     }
+                    l_run[qb] = ls;
                 }
 #pragma unroll
                 for (int db = 0; db < DB; db++)
@@ -404,13 +394,6 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
                     for (int qb = 0; qb < QB; qb++)
                         oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             va[db], pb[qb], oacc[qb][db], 0, 0, 0);
-                if (kSumMfma) {
-                    const bf16x8 ones8 = {one, one, one, one, one, one, one, one};
-#pragma unroll
-                    for (int qb = 0; qb < QB; qb++)
-                        lacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pb[qb], lacc[qb],
-                                                                           0, 0, 0);
-                }
             }
         }
         if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
@@ -425,7 +408,7 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
     // ---- epilogue ---------------------------------------------------------------
 #pragma unroll
     for (int qb = 0; qb < QB; qb++) {
-        const float l_tot = kSumMfma ? lacc[qb][0] : l_run[qb] + lane_xor32(l_run[qb]);
+        const float l_tot = l_run[qb] + lane_xor32(l_run[qb]);
         if (qpos[qb] < 0) continue;
         if (!GROWS) {
             const float inv = 1.0f / l_tot;
