@@ -203,6 +203,9 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             skip = w_first > w_last || kt0 > w_last + p.wr || kt1 < w_first - p.wl;
             need_mask = !(kt0 >= w_last - p.wl && kt1 <= w_first + p.wr && kt1 <= ks.k_hi);
         }
+        // global-row mode: a wave past the last global row has nothing to compute
+        // (with few global tokens most waves of the workgroup)
+        if (GROWS) skip = wave_row0 >= p.n_global;
         const unsigned short* Ks = smem + st * T::STAGE;
         const unsigned short* Vs = Ks + T::K_ELEMS;
         f32x16 s[QB][2];
