@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
         f32x16 (&dp)[2] = dpc[PAR];
         if (need_mask) {
             // element (rb, e) is query q0 + rb*32 + (e>>2)*8 + half*4 + (e&3) and key
-            // `key`: valid when x = query - key + wr lies in [0, wl + wr], the query
+            // `key`: valid when query - key + wr lies in [0, wl + wr], the query
             // is <= q_hi and the key <= kb1
 #pragma unroll
             for (int rb = 0; rb < 2; rb++) {
@@ -765,19 +765,25 @@ __global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf1
                     }
                 }
         } else if (need_mask) {
-            // as in the pipelined step: query - key + wr in [0, wl + wr], query
-            // <= q_hi, key <= kb1
+            // the band: query - key + wr in [0, wl + wr], query <= q_hi, key <=
+            // kb1 (the pipelined step keeps its sign-bit form of the same test:
+            // there this form took more registers and measured slower)
+            // The lane's valid query offsets qo (from q0 + half * 4) form one
+            // interval [lo, hi] (an empty one moved past the tile): one
+            // unsigned range compare and a select per element.
+            {
+                const int q_base = q0 + half * 4;
+                int lo = key - p.wr - q_base;
+                int hi = min(lo + span, q_hi - q_base);
+                if (key > kb1 || hi < lo) lo = hi = 1 << 20;
+                const unsigned width = (unsigned)(hi - lo);
 #pragma unroll
-            for (int rb = 0; rb < 2; rb++) {
-                const int base = q0 + rb * 32 + half * 4 - key + p.wr;
-                const int qlim = q_hi - (q0 + rb * 32 + half * 4);
-                const int kbad = kb1 - key;
+                for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int ro = (e >> 2) * 8 + (e & 3);
-                    const int bad = ((base + ro) | (span - base - ro) | (qlim - ro) | kbad) >> 31;
-                    s[rb][e] += __builtin_bit_cast(float, bad & 0xff800000);
-                }
+                    for (int e = 0; e < 16; e++) {
+                        const int qo = rb * 32 + (e >> 2) * 8 + (e & 3);
+                        if ((unsigned)(qo - lo) > width) s[rb][e] = -INFINITY;
+                    }
             }
         }
         // P and dS of the step's four 16-query steps (8 elements each per lane)
