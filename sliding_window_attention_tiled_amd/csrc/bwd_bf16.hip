@@ -403,14 +403,17 @@ template <int D>
 constexpr bool kDkdvPipelined = D == 128;
 
 template <int D>
-__global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2)) void bwd_dkdv_bf16_kernel(const BwdParams bp) {
+__global__ __launch_bounds__(256, (kDkdvPipelined<D> ? 1 : 2))
+void bwd_dkdv_bf16_kernel(const BwdParams bp) {
     using Q = QTileCfg<D>;
     const FwdParams& p = bp.f;
     constexpr int KC = D / 16;
     constexpr int DB = D / 32;
-    // Three LDS stages.  During step st the dk/dv products read tile st, the
-    // scores of step st + 1 read tile st + 1, and tile st + 2 is stored: the
-    // score MFMAs of the next step then run beside this step's exponentials.
+    // Three LDS stages.  During step st tile st + 2 is staged.  Pipelined
+    // (D = 128): the dk/dv products read tile st and the scores of step st + 1
+    // read tile st + 1, so the next step's score MFMAs run beside this step's
+    // exponentials.  Plain order (D = 64): step st reads tile st only, and
+    // the loads of tile st + 2 have two steps to arrive.
     constexpr int NS = 3;
 
     // per stage: Q tile, dout tile, lse2[BQ], delta[BQ]
