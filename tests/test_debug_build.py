@@ -168,6 +168,43 @@ CASES = [
 ]
 
 
+# The seeded random shapes of the parity suite (GQA 1-8, asymmetric and
+# degenerate windows, dilation, duplicate global tokens, both head dimensions
+# and dtypes) through both builds as well.
+from sliding_window_attention_tiled_amd.inputs import fwd_inputs  # noqa: E402
+from tests.gpu_util import to_dev  # noqa: E402
+from tests.test_random_gpu import BWD_CASES as _RAND_BWD  # noqa: E402
+from tests.test_random_gpu import FWD_CASES as _RAND_FWD  # noqa: E402
+
+
+def _rand_fwd(case):
+    name, B, Hq, Hkv, N, D, dt, wl, wr, dil, G, sc = case
+
+    def run():
+        q, k, v = (to_dev(x) for x in fwd_inputs(1000 + int(name[1:]), B, Hq, Hkv, N, D, dt))
+        out, lse = binding.fwd(q, k, v, win_left=wl, win_right=wr, dilation=dil,
+                               global_idx=G, scale=sc)
+        return [out, lse]
+    return run
+
+
+def _rand_bwd(case):
+    name, B, Hq, Hkv, N, D, dt, wl, wr, dil, G, sc = case
+
+    def run():
+        seed = 2000 + int(name[1:])
+        q, k, v = (to_dev(x) for x in fwd_inputs(seed, B, Hq, Hkv, N, D, dt))
+        g = to_dev(fwd_inputs(seed + 500, B, Hq, Hkv, N, D, dt)[0])
+        kw = dict(win_left=wl, win_right=wr, dilation=dil, global_idx=G, scale=sc)
+        out, lse = binding.fwd(q, k, v, **kw)
+        return [out, lse, *binding.bwd(q, k, v, out, lse, g, **kw)]
+    return run
+
+
+CASES += [(f"random_fwd_{c[0]}", _rand_fwd(c)) for c in _RAND_FWD]
+CASES += [(f"random_bwd_{c[0]}", _rand_bwd(c)) for c in _RAND_BWD]
+
+
 def _same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
     if a.dtype.is_floating_point:
         iv = {2: torch.int16, 4: torch.int32}[a.element_size()]
