@@ -170,11 +170,15 @@ CASES = [
 
 # The seeded random shapes of the parity suite (GQA 1-8, asymmetric and
 # degenerate windows, dilation, duplicate global tokens, both head dimensions
-# and dtypes) through both builds as well.
-from sliding_window_attention_tiled_amd.inputs import fwd_inputs  # noqa: E402
+# and dtypes; ring sizes, fills and sink counts for decode and the chunked
+# prefill) through both builds as well.
+from sliding_window_attention_tiled_amd.inputs import DecodeInputs, fwd_inputs  # noqa: E402
 from tests.gpu_util import to_dev  # noqa: E402
 from tests.test_random_gpu import BWD_CASES as _RAND_BWD  # noqa: E402
+from tests.test_random_gpu import CACHED_CASES as _RAND_CACHED  # noqa: E402
+from tests.test_random_gpu import DECODE_CASES as _RAND_DECODE  # noqa: E402
 from tests.test_random_gpu import FWD_CASES as _RAND_FWD  # noqa: E402
+from tests.test_random_gpu import SINK_CASES as _RAND_SINKS  # noqa: E402
 
 
 def _rand_fwd(case):
@@ -201,8 +205,64 @@ def _rand_bwd(case):
     return run
 
 
+def _dev_ring(gen):
+    return (to_dev(gen.kcache), to_dev(gen.vcache),
+            torch.from_numpy(gen.ring_head.copy()).to("cuda"),
+            torch.from_numpy(gen.cache_len.copy()).to("cuda"))
+
+
+def _rand_decode(case):
+    name, B, Hq, Hkv, W, D, dt, fill = case
+
+    def run():
+        gen = DecodeInputs(3000 + int(name[1:]), B, Hq, Hkv, W, D, dt, fill=fill)
+        kc, vc, head, length = _dev_ring(gen)
+        res = []
+        for _ in range(3):
+            qn, kn, vn = gen.step()
+            binding.kv_append(kc, vc, to_dev(kn), to_dev(vn), head, length)
+            res += list(binding.decode(to_dev(qn), kc, vc, head, length))
+        return res + [kc, vc, head, length]
+    return run
+
+
+def _rand_cached(case):
+    name, B, Hq, Hkv, W, D, dt, fill, n, wl = case
+
+    def run():
+        seed = 4000 + int(name[1:])
+        gen = DecodeInputs(seed, B, 1, Hkv, W, D, dt, fill=fill)
+        q, k, v = (to_dev(x) for x in fwd_inputs(seed + 500, B, Hq, Hkv, n, D, dt))
+        kc, vc, head, length = _dev_ring(gen)
+        out, lse = binding.fwd_cached(q, k, v, kc, vc, head, length, win_left=wl)
+        binding.kv_append_chunk(kc, vc, k, v, head, length)
+        return [out, lse, kc, vc, head, length]
+    return run
+
+
+def _rand_sinks(case):
+    from tests.test_sinks_gpu import _sinks
+    name, B, Hq, Hkv, W, D, dt, fill, S = case
+
+    def run():
+        seed = 5000 + int(name[1:])
+        gen = DecodeInputs(seed, B, Hq, Hkv, W, D, dt, fill=fill)
+        ks, vs = (to_dev(x) for x in _sinks(seed + 500, B, Hkv, S, D, dt))
+        kc, vc, head, length = _dev_ring(gen)
+        res = []
+        for _ in range(2):
+            qn, kn, vn = gen.step()
+            binding.kv_append(kc, vc, to_dev(kn), to_dev(vn), head, length)
+            res += list(binding.decode_sinks(to_dev(qn), kc, vc, head, length, ks, vs))
+        return res
+    return run
+
+
 CASES += [(f"random_fwd_{c[0]}", _rand_fwd(c)) for c in _RAND_FWD]
 CASES += [(f"random_bwd_{c[0]}", _rand_bwd(c)) for c in _RAND_BWD]
+CASES += [(f"random_decode_{c[0]}", _rand_decode(c)) for c in _RAND_DECODE]
+CASES += [(f"random_cached_{c[0]}", _rand_cached(c)) for c in _RAND_CACHED]
+CASES += [(f"random_sinks_{c[0]}", _rand_sinks(c)) for c in _RAND_SINKS]
 
 
 def _same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
