@@ -35,6 +35,44 @@ def _normal_bf16(shape, gen):
     return x
 
 
+# (the ring test runs first and frees its 64 GiB before the forward tests draw
+# their 96 GiB of inputs, so that at most about 130 GiB are held at once)
+def test_append_and_decode_on_max_ring():
+    torch.cuda.empty_cache()
+    B, Hq, Hkv, W, D = 1, 8, 1, SWA_MAX_N, 64
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    log("[maxsize] ring of 2^28 slots: drawing K and V")
+    kc = _normal_bf16((B, Hkv, W, D), gen)
+    vc = _normal_bf16((B, Hkv, W, D), gen)
+    head = torch.tensor([2000], dtype=torch.int32, device="cuda")
+    length = torch.tensor([4999], dtype=torch.int32, device="cuda")
+    k_new = _normal_bf16((B, Hkv, D), gen)
+    v_new = _normal_bf16((B, Hkv, D), gen)
+    binding.kv_append(kc, vc, k_new, v_new, head, length)
+    torch.cuda.synchronize()
+    assert head.cpu().tolist() == [2001] and length.cpu().tolist() == [5000]
+    assert torch.equal(kc[0, 0, 2000].view(torch.int16), k_new[0, 0].view(torch.int16))
+    assert torch.equal(vc[0, 0, 2000].view(torch.int16), v_new[0, 0].view(torch.int16))
+    q = _normal_bf16((B, Hq, D), gen)
+    log("[maxsize] decode over 5000 live entries wrapping slot 0 of a 2^28-slot ring")
+    out, lse = binding.decode(q, kc, vc, head, length)
+    torch.cuda.synchronize()
+    # the live entries in age order (age a at slot (head - 1 - a) mod W), as a
+    # ring of their own: W' = 5000, head' = 0, age a at slot 4999 - a
+    L = 5000
+    ages = torch.arange(L, device="cuda")
+    slots = (2001 - 1 - ages) % W
+    order = torch.flip(slots, [0])          # slot of age L-1-j at position j
+    ks = _bits(kc[:, :, order])
+    vs = _bits(vc[:, :, order])
+    ring = oracle.ring(ks, vs, np.array([0], np.int32), np.array([L], np.int32))
+    ref_o, ref_l = ring.decode(_bits(q))
+    check(to_host_f64(out), ref_o, "bf16", "2^28-slot ring decode out")
+    check(to_host_f64(lse), ref_l, "bf16", "2^28-slot ring decode lse")
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
 @pytest.fixture(scope="module")
 def big_qkv():
     torch.cuda.empty_cache()
@@ -87,39 +125,3 @@ def test_fwd_at_max_sequence_length_dilated_bidirectional(big_qkv):
     torch.cuda.synchronize()
     _check_rows(q, k, v, out, lse, _rows(SWA_MAX_N, 2), 40, 30, 3, "N = 2^28 dilated")
     del out, lse
-
-
-def test_append_and_decode_on_max_ring():
-    torch.cuda.empty_cache()
-    B, Hq, Hkv, W, D = 1, 8, 1, SWA_MAX_N, 64
-    gen = torch.Generator(device="cuda").manual_seed(77)
-    log("[maxsize] ring of 2^28 slots: drawing K and V")
-    kc = _normal_bf16((B, Hkv, W, D), gen)
-    vc = _normal_bf16((B, Hkv, W, D), gen)
-    head = torch.tensor([2000], dtype=torch.int32, device="cuda")
-    length = torch.tensor([4999], dtype=torch.int32, device="cuda")
-    k_new = _normal_bf16((B, Hkv, D), gen)
-    v_new = _normal_bf16((B, Hkv, D), gen)
-    binding.kv_append(kc, vc, k_new, v_new, head, length)
-    torch.cuda.synchronize()
-    assert head.cpu().tolist() == [2001] and length.cpu().tolist() == [5000]
-    assert torch.equal(kc[0, 0, 2000].view(torch.int16), k_new[0, 0].view(torch.int16))
-    assert torch.equal(vc[0, 0, 2000].view(torch.int16), v_new[0, 0].view(torch.int16))
-    q = _normal_bf16((B, Hq, D), gen)
-    log("[maxsize] decode over 5000 live entries wrapping slot 0 of a 2^28-slot ring")
-    out, lse = binding.decode(q, kc, vc, head, length)
-    torch.cuda.synchronize()
-    # the live entries in age order (age a at slot (head - 1 - a) mod W), as a
-    # ring of their own: W' = 5000, head' = 0, age a at slot 4999 - a
-    L = 5000
-    ages = torch.arange(L, device="cuda")
-    slots = (2001 - 1 - ages) % W
-    order = torch.flip(slots, [0])          # slot of age L-1-j at position j
-    ks = _bits(kc[:, :, order])
-    vs = _bits(vc[:, :, order])
-    ring = oracle.ring(ks, vs, np.array([0], np.int32), np.array([L], np.int32))
-    ref_o, ref_l = ring.decode(_bits(q))
-    check(to_host_f64(out), ref_o, "bf16", "2^28-slot ring decode out")
-    check(to_host_f64(lse), ref_l, "bf16", "2^28-slot ring decode lse")
-    del kc, vc
-    torch.cuda.empty_cache()
