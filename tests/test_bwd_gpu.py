@@ -85,6 +85,13 @@ GLOBAL_CASES = [
     ("g_window_ge_n", 1, 4, 2, 90, 128, "bf16", 200, 200, 1, None, [0, 45, 89]),
     # three tokens, one global, causal
     ("g_tiny_n", 1, 2, 2, 3, 64, "bf16", 1, 0, 1, None, [1]),
+    # D = 64 bf16, where the band passes take the global pairs themselves:
+    # causal with dilation (global rows and keys in every residue class), and
+    # 84 globals (two gathered tiles per head in both passes)
+    ("g_causal_dil3_gqa2_d64", 1, 4, 2, 420, 64, "bf16", 25, 0, 3, None,
+     [0, 1, 2, 64, 65, 200, 301, 419]),
+    ("g_many_causal_dil2_d64", 1, 4, 2, 500, 64, "bf16", 40, 0, 2, None,
+     list(range(1, 500, 6))),
 ]
 
 
