@@ -11,7 +11,7 @@
 //     query head of the kv head's group),
 //     dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i.
 // P is rebuilt from the forward's lse; delta_i = dout_i . out_i comes from the
-// bf16 file's delta kernel.
+// delta kernel in bwd_bf16.hip (its float32 instance).
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
