@@ -40,7 +40,10 @@ struct TileCfg {
 // no window reaches) in gk[2][BN], for the element masks.  Band tiles that
 // start at a negative coordinate (chunked prefill) take those keys from the
 // ring rows krbase / vrbase (row pitch D).
-template <class T, bool GROWS>
+// PLAIN: every tile is a run of rows of the key stream (no ring prefix, no
+// gathered global keys), as in the global-row pass and in the band loop of a
+// launch with global tokens (which has no ring).
+template <class T, bool PLAIN>
 __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
                                           u32x4 (&vr)[T::PER_THREAD],
                                           const __bf16* kbase, const __bf16* vbase,
@@ -49,7 +52,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
                                           int j, int* gk, const int* gpos) {
     const int key0 = threadIdx.x / T::CPR;
     const int c = threadIdx.x % T::CPR;
-    if (!GROWS && j < ks.n_band_tiles && ks.k_lo + j * BN < 0) {
+    if (!PLAIN && j < ks.n_band_tiles && ks.k_lo + j * BN < 0) {
         // d = 1 and r = 0 here: coordinate = position within the chunk
         const int kk0 = ks.k_lo + j * BN + key0;
 #pragma unroll
@@ -73,7 +76,7 @@ __device__ __forceinline__ void load_tile(u32x4 (&kr)[T::PER_THREAD],
         }
         return;
     }
-    if (GROWS || j < ks.n_band_tiles) {
+    if (PLAIN || j < ks.n_band_tiles) {
         // band keys past k_hi only occur in the last tile, which is always
         // element-masked: load them from k_hi instead of predicating the loads
         const int kk0 = ks.k_lo + j * BN + key0;
