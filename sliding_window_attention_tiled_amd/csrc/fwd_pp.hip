@@ -67,17 +67,18 @@ __device__ __forceinline__ int chunk_xor(int q) { return V ? 4 * q : q; }
 // 16 bytes per lane from global memory to LDS at m0 + 16 * lane (one wait
 // state between the write of m0 and the load that reads it): from a per-lane
 // address, or from a wave-uniform base plus a per-lane 32-bit byte offset
+// (m0 is declared clobbered: the compiler keeps nothing there across them)
 __device__ __forceinline__ void load_lds_x4(const void* src, unsigned lds_byte) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_byte), "v"(src)
-                 : "memory");
+                 : "memory", "m0");
 }
 __device__ __forceinline__ void load_lds_x4(const void* base, unsigned off, unsigned lds_byte) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_byte), "v"(off), "s"(base)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
