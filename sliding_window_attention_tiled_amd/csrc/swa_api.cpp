@@ -203,8 +203,8 @@ int swa_debug_violations(unsigned long long* count, int reset) {
 #ifdef SWA_DEBUG
     if (hipDeviceSynchronize() != hipSuccess) return SWA_ERR_HIP;
     hipError_t (*const readers[])(unsigned*, bool) = {
-        swa::debug_counter_fwd_bf16, swa::debug_counter_fwd_pp, swa::debug_counter_bwd_bf16,
-        swa::debug_counter_decode};
+        swa::debug_counter_fwd_bf16, swa::debug_counter_fwd_pp, swa::debug_counter_fwd_f32,
+        swa::debug_counter_bwd_bf16, swa::debug_counter_decode};
     unsigned long long total = 0;
     for (auto read : readers) {
         unsigned v = 0;

@@ -197,6 +197,7 @@ hipError_t launch_combine(const CombineParams& p, int D, int dtype, hipStream_t 
 // kernel source file on the current device.
 hipError_t debug_counter_fwd_bf16(unsigned* value, bool reset);
 hipError_t debug_counter_fwd_pp(unsigned* value, bool reset);
+hipError_t debug_counter_fwd_f32(unsigned* value, bool reset);
 hipError_t debug_counter_bwd_bf16(unsigned* value, bool reset);
 hipError_t debug_counter_decode(unsigned* value, bool reset);
 #endif
