@@ -16,7 +16,10 @@
 //   rows_dkdv  dk, dv of every key over E_row, read-modify-write
 //   cols_dq    dq of non-global rows over E_col, read-modify-write
 //   cols_dkdv  dk, dv of global keys over E_col, one float32 partial per row chunk
-//   add_dq / add_dkdv sum the partials in chunk order into dq / dk, dv.
+//   add_dq / add_dkdv sum the partials in chunk order into dq / dk, dv
+//   (in bf16, rows_dkdv, when launched, sums the cols_dkdv partials of the
+//   global keys itself, so that each gradient is rounded once after the band
+//   pass, and add_dkdv is not launched).
 // In bf16 the band dq pass walks the global keys after its band (cols_dq is
 // not launched), and at D = 64 the band dk/dv pass stages the global rows
 // after its band (rows_dkdv is not launched): GlobalBwdParams::fused says
@@ -72,6 +75,19 @@ __device__ __forceinline__ bool in_band(const GlobalBwdParams& g, int i, int j) 
     if (diff % g.dil != 0) return false;
     const int t = diff / g.dil;
     return t >= -g.wl && t <= g.wr;
+}
+
+// index of position j in the sorted global list, -1 if j is not global
+__device__ __forceinline__ int global_index(const GlobalBwdParams& g, int j) {
+    int lo = 0, hi = g.n_global - 1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const int x = g.gpos[mid];
+        if (x == j) return mid;
+        if (x < j) lo = mid + 1;
+        else hi = mid - 1;
+    }
+    return -1;
 }
 
 // the pair is in E_row or E_col (the caller knows which side is global)
@@ -681,6 +697,25 @@ __global__ __launch_bounds__(kMfmaNT) void rows_dkdv_mfma_kernel(const GlobalBwd
         }
     }
     if (!j_ok) return;
+    // A global key also has pairs with the rows outside its band, which
+    // cols_dkdv (launched before this kernel) left as float32 partials.  They
+    // are summed here in chunk order, as add_dkdv would, so that the key's
+    // gradient is rounded to bf16 once after the band pass, not twice.
+    const int gk = global_index(g, j);
+    if (gk >= 0) {
+        const float* part =
+            g.dkv_part + (((size_t)b * g.Hkv + kvh) * g.n_global + gk) * g.n_row_chunks * 2 * D;
+#pragma unroll
+        for (int d = 0; d < DB; d++) {
+            f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < g.n_row_chunks; c++) {
+                sk += *(const f32x4*)(part + (size_t)c * 2 * D + d * 16 + grp * 4);
+                sv += *(const f32x4*)(part + (size_t)c * 2 * D + D + d * 16 + grp * 4);
+            }
+            dkt[d] += sk;
+            dvt[d] += sv;
+        }
+    }
     // dkt[d][e]: dimension 16 d + 4 grp + e of key j
 #pragma unroll
     for (int d = 0; d < DB; d++) {
@@ -978,7 +1013,10 @@ hipError_t launch_all(const GlobalBwdParams& g, hipStream_t s) {
         hipLaunchKernelGGL((rows_dkdv_kernel<D, T>), rows_dkdv_grid, dim3(NT), 0, s, g);
     }
     hipLaunchKernelGGL((add_dq_kernel<D, T>), dim3(blocks_for(nq)), dim3(NT), 0, s, g);
-    hipLaunchKernelGGL((add_dkdv_kernel<D, T>), dim3(blocks_for(nkv / 2)), dim3(NT), 0, s, g);
+    // bf16 rows_dkdv adds the global keys' partials itself
+    const bool dkdv_added = std::is_same_v<T, __bf16> && !(g.fused & kGlobalRowsDkdvFused);
+    if (!dkdv_added)
+        hipLaunchKernelGGL((add_dkdv_kernel<D, T>), dim3(blocks_for(nkv / 2)), dim3(NT), 0, s, g);
     return hipGetLastError();
 }
 

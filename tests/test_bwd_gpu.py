@@ -92,6 +92,13 @@ GLOBAL_CASES = [
      [0, 1, 2, 64, 65, 200, 301, 419]),
     ("g_many_causal_dil2_d64", 1, 4, 2, 500, 64, "bf16", 40, 0, 2, None,
      list(range(1, 500, 6))),
+    # D = 128 bf16, where rows_dkdv adds the global rows' terms to every key and
+    # sums the global keys' partials before its one rounding: many globals, so
+    # that each global key gathers terms from most rows of the sequence
+    ("g_many_bidir_gqa4_d128", 1, 8, 2, 900, 128, "bf16", 48, 48, 1, None,
+     list(range(0, 900, 9))),
+    ("g_many_causal_d128", 1, 4, 1, 800, 128, "bf16", 64, 0, 1, None,
+     list(range(3, 800, 8))),
 ]
 
 
