@@ -19,6 +19,7 @@ and the backward of the headline layer (TFLOP/s at 10*D flop per pair).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
                     [--no-others]
+    python bench.py --power     # board power and shader clock under load (amd-smi)
 """
 from __future__ import annotations
 
@@ -99,6 +100,9 @@ def parse():
     ap.add_argument("--cpu-decode-steps", type=int, default=256)
     ap.add_argument("--only", choices=["fwd", "decode", "others"], default=None,
                     help="run one leg only (for profiling)")
+    ap.add_argument("--power", action="store_true",
+                    help="run only the board-power leg: each workload in a loop for a few "
+                         "seconds while amd-smi samples socket power and shader clocks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -500,6 +504,104 @@ def cpu_baseline_decode(host, n_steps):
     return r
 
 
+def _smi_sample():
+    """Socket power (W) and the shader clock of each XCD (MHz) from amd-smi, or
+    None where the tool is missing or its output has another shape."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+        watts = float(g["power"]["socket_power"]["value"])
+        clks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                if k.startswith("gfx_") and isinstance(v, dict)]
+        return watts, clks
+    except Exception:
+        return None
+
+
+def _power_of(name, fn, seconds=5.0, settle=1.0):
+    """Run fn in a loop for `seconds` while a thread samples amd-smi; samples of
+    the first `settle` seconds (clock ramp) are dropped."""
+    import threading
+    import time
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    samples, stop = [], []
+    t0 = time.time()
+
+    def sampler():
+        while not stop:
+            s = _smi_sample()
+            if s is not None and time.time() - t0 >= settle:
+                samples.append(s)
+            time.sleep(0.25)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    stop.append(1)
+    th.join()
+    rec = {"workload": name, "calls": n, "ms_per_call": round(e0.elapsed_time(e1) / n, 4),
+           "samples": len(samples)}
+    if samples:
+        w = [s[0] for s in samples]
+        c = [sum(s[1]) / len(s[1]) for s in samples if s[1]]
+        rec["socket_power_w"] = round(sum(w) / len(w), 1)
+        rec["socket_power_w_max"] = max(w)
+        if c:
+            rec["gfx_clock_mhz"] = round(sum(c) / len(c), 1)
+            rec["gfx_clock_mhz_min"] = round(min(min(s[1]) for s in samples if s[1]), 1)
+    return rec
+
+
+def bench_power():
+    """Board power and shader clock under each heavy workload: the headline
+    forward, its backward and the bidirectional encoder forward with global
+    tokens; and the idle board for reference."""
+    import time
+    import torch
+    from sliding_window_attention_tiled_amd import binding, configs
+    from sliding_window_attention_tiled_amd.inputs import fwd_inputs
+
+    out = []
+    idle = _smi_sample()
+    if idle is not None:
+        out.append({"workload": "idle", "socket_power_w": idle[0],
+                    "gfx_clock_mhz": round(sum(idle[1]) / max(1, len(idle[1])), 1)})
+    for name in ("mistral_causal_w4096", "bidir_encoder_globals"):
+        c = configs.FWD[name]
+        q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["N"],
+                                                 c["D"], c["dtype"]))
+        kw = dict(win_left=c["win_left"], win_right=c["win_right"], dilation=c["dilation"],
+                  global_idx=c.get("global_idx"))
+        o = torch.empty_like(q)
+        lse = torch.empty((c["B"], c["Hq"], c["N"]), dtype=torch.float32, device="cuda")
+        out.append(_power_of(name, lambda: binding.fwd(q, k, v, out=o, lse=lse, **kw)))
+        if name == "mistral_causal_w4096":
+            g = to_dev(fwd_inputs(c["seed"] + 100, c["B"], c["Hq"], c["Hkv"], c["N"], c["D"],
+                                  c["dtype"])[0])
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            out.append(_power_of("bwd_" + name,
+                                 lambda: binding.bwd(q, k, v, o, lse, g, dq=dq, dk=dk, dv=dv,
+                                                     **kw)))
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+        time.sleep(1.0)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -513,6 +615,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.power:
+        print(json.dumps({"power": bench_power()}))
         return
     if args.only == "decode":
         print(json.dumps({"decode": bench_decode(args)[0]}))
