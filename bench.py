@@ -11,7 +11,9 @@ K+V streamed, and the fp64 CPU oracle timed on bounded samples of both
 (forward rows as TFLOP/s, decode steps as GB/s), with the host's CPU count
 and model.
 
-Also reported, per call: the bidirectional encoder with global tokens, the
+Also reported: socket power and shader clock while the forward runs in a
+loop for 3 s (amd-smi), with the MFMA peak at that clock.  Per call: the
+bidirectional encoder with global tokens, the
 four layers of the dilated stack and one 4096-token chunk of a chunked prefill
 (exact TFLOP/s against min(MFMA peak, HBM peak x arithmetic intensity)), and
 the decode shape with four attention sinks and through a paged pool (GB/s),
@@ -521,6 +523,19 @@ def _smi_sample():
         return None
 
 
+def _power_cap():
+    """The board's power cap in W (rocm-smi --showmaxpower), or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True,
+                           timeout=20)
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", r.stdout)
+        return float(m.group(1)) if m else None
+    except Exception:
+        return None
+
+
 def _power_of(name, fn, seconds=5.0, settle=1.0):
     """Run fn in a loop for `seconds` while a thread samples amd-smi; samples of
     the first `settle` seconds (clock ramp) are dropped."""
@@ -575,7 +590,7 @@ def bench_power():
     from sliding_window_attention_tiled_amd import binding, configs
     from sliding_window_attention_tiled_amd.inputs import fwd_inputs
 
-    out = []
+    out = [{"power_cap_w": _power_cap()}]
     idle = _smi_sample()
     if idle is not None:
         out.append({"workload": "idle", "socket_power_w": idle[0],
@@ -600,6 +615,34 @@ def bench_power():
         torch.cuda.empty_cache()
         time.sleep(1.0)
     return out
+
+
+def board_under_fwd(seconds=3.0):
+    """Socket power and shader clock while the headline forward runs in a loop,
+    and the bf16 MFMA peak at that clock (the published peak is counted at
+    2.4 GHz); empty where amd-smi gives nothing."""
+    import torch
+    from sliding_window_attention_tiled_amd import binding, configs
+    from sliding_window_attention_tiled_amd.inputs import fwd_inputs
+
+    c = configs.FWD["mistral_causal_w4096"]
+    q, k, v = (to_dev(x) for x in fwd_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["N"],
+                                             c["D"], c["dtype"]))
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["Hq"], c["N"]), dtype=torch.float32, device="cuda")
+    rec = _power_of("mistral_causal_w4096",
+                    lambda: binding.fwd(q, k, v, win_left=c["win_left"], out=o, lse=lse),
+                    seconds=seconds)
+    if "gfx_clock_mhz" not in rec:
+        return {}
+    peak = PEAK_BF16_TFLOPS * rec["gfx_clock_mhz"] / 2400.0
+    W = c["win_left"] + 1
+    exact = 4.0 * c["B"] * c["Hq"] * exact_pairs_causal(c["N"], W) * c["D"]
+    tf = exact / (rec["ms_per_call"] * 1e-3) / 1e12
+    return {"socket_power_w": rec["socket_power_w"], "power_cap_w": _power_cap(),
+            "gfx_clock_mhz": rec["gfx_clock_mhz"], "ms_per_call": rec["ms_per_call"],
+            "mfma_peak_at_clock_tflops": round(peak, 1),
+            "frac_of_peak_at_clock": round(tf / peak, 4)}
 
 
 def main():
@@ -650,6 +693,10 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(exact_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic()},
     }
+    if args.only is None:
+        board = board_under_fwd()
+        if board:
+            res["board_under_fwd"] = board
     dec_host = None
     if not args.no_decode and args.only is None:
         res["decode"], dec_host = bench_decode(args)
