@@ -338,21 +338,25 @@ void swa_fwd_bf16_kernel(const FwdParams p) {
             // weights (B operand of P V) and their sum
 #pragma unroll
             for (int qb = 0; qb < QB; qb++) {
-                float mx = s[qb][0][0];
+                // the lane's own 32 keys first: only if some lane of the wave
+                // passes the running max by more than the lazy bound is the max
+                // exchanged with lane ^ 32 (otherwise every row keeps its max,
+                // as the exchanged max would have decided too)
+                float lmx = s[qb][0][0];
 #pragma unroll
-                for (int e = 1; e < 16; e++) mx = fmaxf(mx, s[qb][0][e]);
+                for (int e = 1; e < 16; e++) lmx = fmaxf(lmx, s[qb][0][e]);
 #pragma unroll
-                for (int e = 0; e < 16; e++) mx = fmaxf(mx, s[qb][1][e]);
-                mx = wave_max_xor32(mx) * c;
-                const bool up = mx > m_run[qb] + kLazyRescale;
-                m_use[qb] = up ? mx : m_run[qb];
-                if (__any(up)) {
-                    const float alpha = fast_exp2(m_run[qb] - m_use[qb]);
+                for (int e = 0; e < 16; e++) lmx = fmaxf(lmx, s[qb][1][e]);
+                if (__any(lmx * c > m_run[qb] + kLazyRescale)) {
+                    const float mx = wave_max_xor32(lmx) * c;
+                    const float m_new = mx > m_run[qb] + kLazyRescale ? mx : m_run[qb];
+                    const float alpha = fast_exp2(m_run[qb] - m_new);
                     l_run[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; db++) oacc[qb][db] *= alpha;
+                    m_run[qb] = m_new;
                 }
-                m_run[qb] = m_use[qb];
+                m_use[qb] = m_run[qb];
             }
             // O^T += V^T P^T : four 16-key steps; V^T through transposing reads
             // At D = 128 a wave takes issue priority over the other wave on its
