@@ -384,17 +384,20 @@ __global__ __launch_bounds__(512, 1) void swa_fwd_pp_kernel(const FwdParams p) {
             const float m4c = max3(m11[6], m11[7], m11[8]);
             const float m4d = max3(m11[9], m11[10], m11[10]);
             const float mlane = max3(max3(m4a, m4b, m4c), m4d, m4d);
-            const float mx = wave_max_xor32(mlane) * c;
-            const bool up = mx > m_run + kLazyRescale;
-            const float m_use = up ? mx : m_run;
-            if (__any(up)) {
-                const float alpha = fast_exp2(m_run - m_use);
+            // the max is exchanged with lane ^ 32 only when some lane's own keys
+            // pass the running max by more than the lazy bound (otherwise every
+            // row keeps its max, as the exchanged max would have decided too)
+            if (__any(mlane * c > m_run + kLazyRescale)) {
+                const float mx = wave_max_xor32(mlane) * c;
+                const float m_new = mx > m_run + kLazyRescale ? mx : m_run;
+                const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
                 for (int tt = 0; tt < 4; tt++) l_part[tt] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; db++) oacc[db] *= alpha;
+                m_run = m_new;
             }
-            m_run = m_use;
+            const float m_use = m_run;
 #pragma unroll
             for (int tt = 0; tt < 4; tt++) {
 #pragma unroll
